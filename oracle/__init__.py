@@ -1,0 +1,139 @@
+"""CPU oracle for the N-way TREDUCE reduction -- test infrastructure only.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package.  The product library and its Python
+binding never import, load or call it, and it shares no code with them.
+
+The arithmetic lives in ``treduce_oracle.c`` (plain loops, one element at a
+time, in the order of "CANN PTO-ISA TREDUCE instruction explained" §4.3);
+this module compiles it with gcc and marshals numpy arrays into it.
+
+Element buffers are passed as numpy arrays of the raw element bits:
+``float32`` for f32, ``int32`` for i32, ``uint16`` for bf16 and f16.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "treduce_oracle.c")
+_LIB = os.path.join(_HERE, "libtreduce_oracle.so")
+
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "i32": 3}
+OPS = {"sum": 0, "max": 1, "min": 2, "prod": 3}
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16, "i32": np.int32}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (IEEE arithmetic: no contraction, no fast-math)."""
+    cmd = [
+        "gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+        "-fno-finite-math-only", "-Wall", "-Wextra", "-shared", "-fPIC",
+        "-o", _LIB + ".tmp", _SRC, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    lib.oracle_treduce.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, vp,
+                                   i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_treduce.restype = ctypes.c_int
+    lib.oracle_allreduce_inplace.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, vp,
+                                             i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_allreduce_inplace.restype = ctypes.c_int
+    lib.oracle_combine_bits.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, i64]
+    lib.oracle_combine_bits.restype = None
+    lib.oracle_round_from_double.argtypes = [ctypes.c_int, vp, vp, i64]
+    lib.oracle_round_from_double.restype = None
+    lib.oracle_to_double.argtypes = [ctypes.c_int, vp, vp, i64]
+    lib.oracle_to_double.restype = None
+    lib.oracle_max_ranks.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check_buffers(arrs: Sequence[np.ndarray], dtype: str, rows: int, ld: int, cols: int):
+    need = (rows - 1) * ld + cols if rows > 0 else 0
+    for a in arrs:
+        if a.dtype != STORAGE[dtype]:
+            raise TypeError(f"oracle buffer dtype {a.dtype} does not hold {dtype}")
+        if not a.flags.c_contiguous:
+            raise ValueError("oracle buffers must be C-contiguous")
+        if a.size < need:
+            raise ValueError(f"oracle buffer of {a.size} elements is smaller than {need}")
+
+
+def treduce(srcs: Sequence[np.ndarray], dst: np.ndarray, *, root: int, dtype: str, op: str,
+            rows: int, cols: int, ld: int, valid_rows: int, valid_cols: int) -> None:
+    """dst[i*ld+j] = (+)_r srcs[r][i*ld+j] over the valid rectangle, in place in ``dst``."""
+    lib = _load()
+    _check_buffers(list(srcs) + [dst], dtype, rows, ld, cols)
+    ptrs = (ctypes.c_void_p * max(1, len(srcs)))(*[a.ctypes.data for a in srcs])
+    rc = lib.oracle_treduce(ptrs, len(srcs), root, dst.ctypes.data, rows, cols, ld,
+                            valid_rows, valid_cols, DTYPES[dtype], OPS[op])
+    if rc != 0:
+        raise ValueError(f"oracle_treduce rejected its arguments (status {rc})")
+
+
+def allreduce_inplace(bufs: Sequence[np.ndarray], *, root: int, dtype: str, op: str, rows: int,
+                      cols: int, ld: int, valid_rows: int, valid_cols: int) -> None:
+    """Reduce all buffers and write the result back into every one of them."""
+    lib = _load()
+    _check_buffers(bufs, dtype, rows, ld, cols)
+    scratch = np.zeros_like(bufs[0])
+    ptrs = (ctypes.c_void_p * len(bufs))(*[a.ctypes.data for a in bufs])
+    rc = lib.oracle_allreduce_inplace(ptrs, len(bufs), root, scratch.ctypes.data, rows, cols,
+                                      ld, valid_rows, valid_cols, DTYPES[dtype], OPS[op])
+    if rc != 0:
+        raise ValueError(f"oracle_allreduce_inplace rejected its arguments (status {rc})")
+
+
+def combine_bits(dtype: str, op: str, a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """One combine step on raw element bits held in uint32 arrays."""
+    lib = _load()
+    a = np.ascontiguousarray(a, dtype=np.uint32)
+    b = np.ascontiguousarray(b, dtype=np.uint32)
+    out = np.empty_like(a)
+    lib.oracle_combine_bits(DTYPES[dtype], OPS[op], a.ctypes.data, b.ctypes.data,
+                            out.ctypes.data, a.size)
+    return out
+
+
+def round_from_double(dtype: str, x: np.ndarray) -> np.ndarray:
+    """Nearest element of a float dtype to each double, ties to even; uint32 bits."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint32)
+    lib.oracle_round_from_double(DTYPES[dtype], x.ctypes.data, out.ctypes.data, x.size)
+    return out
+
+
+def to_double(dtype: str, bits: np.ndarray) -> np.ndarray:
+    """Exact value of each element's bits (uint32 holding the element)."""
+    lib = _load()
+    bits = np.ascontiguousarray(bits, dtype=np.uint32)
+    out = np.empty(bits.shape, dtype=np.float64)
+    lib.oracle_to_double(DTYPES[dtype], bits.ctypes.data, out.ctypes.data, bits.size)
+    return out
+
+
+def max_ranks() -> int:
+    return int(_load().oracle_max_ranks())
