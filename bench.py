@@ -1,0 +1,207 @@
+"""Benchmark of the N-way reduction on one MI355X.
+
+One step = one ptored_treduce call over the whole workload (every source
+read once, dst written once), inputs resident in HBM.  Prints ONE JSON line:
+effective HBM GB/s = (N+1) * valid bytes / time, with the roofline of the
+reduce kernel and the CPU oracle timed on a bounded sample as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--op OP]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "cross_rank_collective_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; the stored HBM counter readings are only
+    quoted while the kernels are the ones they were taken on."""
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(CSRC)):
+        if fn.endswith((".cuh", ".hip", ".h")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(CSRC, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, op: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none for this kernel source."""
+    path = os.path.join(PROFILES, f"traffic_{workload}_{op}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, op, srcs, gpu_dst_bits, target_s: float = 10.0):
+    """Time the oracle (single thread, as written) on the first rows of the
+    same workload, sized to about `target_s` seconds, and check the GPU rows
+    against it bit for bit."""
+    import oracle
+    from cross_rank_collective_amd import workloads as W
+
+    def run(rows):
+        size = (rows - 1) * w.ld + w.cols
+        sub = [np.ascontiguousarray(s[:size]) for s in srcs]
+        dst = W.sentinel_buffer(w.dtype, size)
+        t0 = time.perf_counter()
+        oracle.treduce(sub, dst, root=w.root, dtype=w.dtype, op=op, rows=rows, cols=w.cols,
+                       ld=w.ld, valid_rows=rows, valid_cols=w.valid_cols)
+        return time.perf_counter() - t0, dst
+
+    probe_rows = min(w.valid_rows, 8)
+    t_probe, _ = run(probe_rows)
+    rows = int(min(w.valid_rows, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
+    t, dst = run(rows)
+    nbytes = (w.nranks + 1) * rows * w.valid_cols * w.esize
+    m = np.zeros((rows, w.ld), dtype=bool)
+    m[:, :w.valid_cols] = True
+    m = m.reshape(-1)[:dst.size]
+    gpu = gpu_dst_bits[:dst.size]
+    same = np.array_equal(gpu.view(np.uint8).reshape(dst.size, -1)[m],
+                          dst.view(np.uint8).reshape(dst.size, -1)[m])
+    return {
+        "value": round(nbytes / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {rows} of {w.valid_rows} valid rows ({rows * w.valid_cols} elements x "
+                  f"{w.nranks} ranks), {t:.2f} s on 1 thread of {cpu_model()}",
+        "seconds": round(t, 3),
+        "gpu_rows_bit_exact": bool(same),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--op", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the reduction; runs on more than one GPU "
+              "are not supported (use --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from cross_rank_collective_amd import binding as B
+    from cross_rank_collective_amd import workloads as W
+
+    name = args.workload or W.HEADLINE
+    w = W.WORKLOADS[name]
+    op = args.op or w.ops[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.load()
+
+    srcs = W.make_sources(w)
+    src_t = [torch.from_numpy(s.view(np.uint8)).to(dev) for s in srcs]
+    dst_t = torch.full((w.buffer_elems * w.esize,), 0xFF, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = [t.data_ptr() for t in src_t]
+
+    def step():
+        st = B.ptored_treduce(ptrs, w.nranks, w.root, dst_t.data_ptr(), w.rows, w.cols, w.ld,
+                              w.valid_rows, w.valid_cols, B.DTYPES[w.dtype], B.OPS[op],
+                              stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(B.ptored_status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    algo_bytes = w.algorithmic_bytes
+    gbs = algo_bytes / (ms_step * 1e-3) / 1e9
+    elems_s = w.valid_rows * w.valid_cols / (ms_step * 1e-3)
+
+    traffic = stored_traffic(name, op)
+    line = {
+        "metric": "effective HBM GB/s ((N+1)*valid bytes / time) and % of MI355X peak",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": name, "op": op, "nranks": w.nranks, "rows": w.rows, "cols": w.cols,
+            "ld": w.ld, "valid_rows": w.valid_rows, "valid_cols": w.valid_cols, "root": w.root,
+            "values": w.recipe, "algorithmic_bytes_per_step": algo_bytes,
+        },
+        "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "elements_per_s": round(elems_s, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "treduce_vec_kernel",
+            "kernel_source_hash": kernel_source_hash(),
+        },
+    }
+    if not args.no_cpu_baseline:
+        gpu_bits = dst_t.cpu().numpy().view(W.STORAGE[w.dtype])
+        line["cpu_baseline"] = cpu_baseline(w, op, srcs, gpu_bits)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

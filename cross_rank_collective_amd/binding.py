@@ -1,0 +1,182 @@
+"""ctypes binding of libptored.so (argument marshalling only).
+
+Every step of the reduction runs in the library's HIP kernels; this module
+only turns Python values and torch tensors into the C ABI's pointers and
+sizes.  torch provides device memory and the stream.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+
+The C functions keep their names: ``ptored_treduce``, ``ptored_treduce_ex``,
+``ptored_treduce_plan``, ``ptored_status_string``, ``ptored_abi_version``,
+``ptored_max_ranks``.  ``treduce`` is the tensor-level convenience wrapper.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libptored.so")
+
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "i32": 3}
+OPS = {"sum": 0, "max": 1, "min": 2, "prod": 3}
+
+PTORED_OK = 0
+PTORED_ERR_INVALID_ARG = -1
+PTORED_ERR_UNSUPPORTED = -2
+PTORED_ERR_OVERLAP = -3
+PTORED_ERR_HIP = -4
+
+PTORED_FORCE_ELEMENTWISE = 0x1
+PTORED_FORCE_ROWS = 0x2
+PTORED_FORCE_RUNTIME_N = 0x4
+PTORED_NO_XCD_REMAP = 0x8
+PTORED_NT_LOADS = 0x10
+
+PATHS = {0: "none", 1: "copy", 2: "vec_fixed", 3: "vec_runtime", 4: "elementwise"}
+
+
+class ptored_tuning(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("blocks_per_cu", ctypes.c_int32),
+                ("max_launch_bytes", ctypes.c_int64)]
+
+
+class ptored_plan_info(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("rows_mode", ctypes.c_int32),
+                ("vec_elems", ctypes.c_int32), ("slots_per_thread", ctypes.c_int32),
+                ("slots", ctypes.c_int64), ("launches", ctypes.c_int64)]
+
+
+class PtoredError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libptored.so (after torch, so one HIP runtime serves both)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- maps torch's libamdhip64 first
+
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m cross_rank_collective_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    common = [ctypes.POINTER(vp), i32, i32, vp, i64, i64, i64, i64, i64, i32, i32]
+    lib.ptored_treduce.argtypes = common + [vp]
+    lib.ptored_treduce.restype = i32
+    lib.ptored_treduce_ex.argtypes = common + [ctypes.POINTER(ptored_tuning), vp]
+    lib.ptored_treduce_ex.restype = i32
+    lib.ptored_treduce_plan.argtypes = common + [ctypes.POINTER(ptored_tuning),
+                                                 ctypes.POINTER(ptored_plan_info)]
+    lib.ptored_treduce_plan.restype = i32
+    lib.ptored_status_string.argtypes = [i32]
+    lib.ptored_status_string.restype = ctypes.c_char_p
+    lib.ptored_abi_version.restype = i32
+    lib.ptored_max_ranks.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptrs(srcs: Sequence[int]):
+    return (ctypes.c_void_p * max(1, len(srcs)))(*[int(p) for p in srcs])
+
+
+def ptored_treduce(srcs: Sequence[int], nranks: int, root: int, dst: int, rows: int, cols: int,
+                   ld: int, valid_rows: int, valid_cols: int, dtype: int, op: int,
+                   stream: int) -> int:
+    """Raw call: device pointers as ints; returns the status code."""
+    return load().ptored_treduce(_ptrs(srcs), nranks, root, dst, rows, cols, ld, valid_rows,
+                                 valid_cols, dtype, op, stream)
+
+
+def ptored_treduce_ex(srcs: Sequence[int], nranks: int, root: int, dst: int, rows: int,
+                      cols: int, ld: int, valid_rows: int, valid_cols: int, dtype: int, op: int,
+                      tuning: Optional[ptored_tuning], stream: int) -> int:
+    t = ctypes.byref(tuning) if tuning is not None else None
+    return load().ptored_treduce_ex(_ptrs(srcs), nranks, root, dst, rows, cols, ld, valid_rows,
+                                    valid_cols, dtype, op, t, stream)
+
+
+def ptored_treduce_plan(srcs: Sequence[int], nranks: int, root: int, dst: int, rows: int,
+                        cols: int, ld: int, valid_rows: int, valid_cols: int, dtype: int,
+                        op: int, tuning: Optional[ptored_tuning] = None
+                        ) -> Tuple[int, ptored_plan_info]:
+    info = ptored_plan_info()
+    t = ctypes.byref(tuning) if tuning is not None else None
+    st = load().ptored_treduce_plan(_ptrs(srcs), nranks, root, dst, rows, cols, ld, valid_rows,
+                                    valid_cols, dtype, op, t, ctypes.byref(info))
+    return st, info
+
+
+def ptored_status_string(status: int) -> str:
+    return load().ptored_status_string(status).decode()
+
+
+def ptored_abi_version() -> int:
+    return load().ptored_abi_version()
+
+
+def ptored_max_ranks() -> int:
+    return load().ptored_max_ranks()
+
+
+def tuning(flags: int = 0, blocks_per_cu: int = 0, max_launch_bytes: int = 0) -> ptored_tuning:
+    return ptored_tuning(flags, blocks_per_cu, max_launch_bytes)
+
+
+def _torch_dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2, torch.int32: 3}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected f32, bf16, f16 or i32")
+    return codes[t.dtype]
+
+
+def _geometry(t) -> Tuple[int, int, int]:
+    if t.dim() == 1:
+        return 1, t.shape[0], t.shape[0]
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("tensors must be 1-D or 2-D row-major with unit column stride")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def treduce(srcs, dst, op: str = "sum", root: int = 0,
+            valid: Optional[Tuple[int, int]] = None, tuning: Optional[ptored_tuning] = None,
+            stream=None) -> None:
+    """dst = fold of the source tensors over the valid rectangle, on the GPU.
+
+    All tensors are on the current device with one dtype and one 2-D
+    row-major geometry (``rows = size(0)``, ``cols = size(1)``,
+    ``ld = stride(0)``).  ``valid`` defaults to the whole tensor.  The call is
+    asynchronous on ``stream`` (default: torch's current stream).
+    """
+    import torch
+
+    if len(srcs) == 0:
+        raise ValueError("treduce needs at least one source")
+    dt = _torch_dtype_code(dst)
+    geo = _geometry(dst)
+    for s in srcs:
+        if s.dtype != dst.dtype or _geometry(s) != geo:
+            raise ValueError("every source must match dst in dtype and geometry")
+        if not s.is_cuda or s.device != dst.device:
+            raise ValueError("every tensor must be on dst's GPU")
+    rows, cols, ld = geo
+    vr, vc = (rows, cols) if valid is None else valid
+    if stream is None:
+        stream = torch.cuda.current_stream(dst.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(dst.device):
+        st = ptored_treduce_ex([s.data_ptr() for s in srcs], len(srcs), root, dst.data_ptr(),
+                               rows, cols, ld, vr, vc, dt, OPS[op], tuning, handle)
+    if st != PTORED_OK:
+        raise PtoredError(st, ptored_status_string(st))

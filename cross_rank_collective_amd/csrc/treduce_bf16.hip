@@ -1,0 +1,10 @@
+// treduce_bf16.hip -- kernel instances and launcher for bf16 elements.
+#include "treduce_launch.cuh"
+
+namespace ptored {
+
+int launch_bf16(const Plan& p, const KArgs& a, int cu_count, hipStream_t stream) {
+    return dispatch_dtype<PTORED_BF16, 2>(p, a, cu_count, stream);
+}
+
+}  // namespace ptored

@@ -1,0 +1,329 @@
+// treduce_host.cpp -- C ABI of the N-way reduction: validation, plan, launch.
+//
+// Sources (cited by title and section):
+//   [TREDUCE]  "CANN PTO-ISA TREDUCE instruction explained" (lpnh.cn article
+//              on pto-isa): §3.3 group checks (size > 0, root in range,
+//              shared shape and strides), §4.1 dispatch (empty region
+//              returns at once; data that fits takes the simple path, else
+//              the chunked walk), §4.3 fold order and the single-rank copy.
+//   [N6]       "Distributed Operators (N6)", PyPTO docs: append-only ABI
+//              enums; pld.tensor.allreduce works in place on the window.
+//
+// Every argument check runs before the first HIP call, so every error status
+// is reachable without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+
+#include "ptored.h"
+#include "treduce_plan.h"
+
+namespace ptored {
+namespace {
+
+int esize_of(int dtype) { return (dtype == PTORED_F32 || dtype == PTORED_I32) ? 4 : 2; }
+
+constexpr int64_t kDefaultLaunchBytes = int64_t(1) << 31;
+constexpr int64_t kMaxElems = int64_t(1) << 60;
+
+// Byte extent [p, p + span) that the valid rectangle touches in one buffer.
+int64_t valid_span_bytes(int64_t vr, int64_t vc, int64_t ld, int es) {
+    if (vr == 0 || vc == 0) return 0;
+    return ((vr - 1) * ld + vc) * es;
+}
+
+int validate(const void* const* srcs, int nranks, int root, const void* dst, int64_t rows,
+             int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols, int dtype,
+             int op) {
+    if (nranks < 1 || nranks > PTORED_MAX_RANKS) return PTORED_ERR_INVALID_ARG;
+    if (root < 0 || root >= nranks) return PTORED_ERR_INVALID_ARG;
+    if (srcs == nullptr || dst == nullptr) return PTORED_ERR_INVALID_ARG;
+    for (int r = 0; r < nranks; ++r)
+        if (srcs[r] == nullptr) return PTORED_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0 || ld < 0 || valid_rows < 0 || valid_cols < 0)
+        return PTORED_ERR_INVALID_ARG;
+    if (cols > ld || valid_rows > rows || valid_cols > cols) return PTORED_ERR_INVALID_ARG;
+    if (rows > 0 && ld > 0 && rows > kMaxElems / ld) return PTORED_ERR_INVALID_ARG;
+    if (dtype < PTORED_F32 || dtype > PTORED_I32) return PTORED_ERR_UNSUPPORTED;
+    if (op < PTORED_SUM || op > PTORED_PROD) return PTORED_ERR_UNSUPPORTED;
+    // dst may be exactly a source (in place: each element is read by the one
+    // thread that later writes it); any other overlap is a race.
+    const int es = esize_of(dtype);
+    const int64_t span = valid_span_bytes(valid_rows, valid_cols, ld, es);
+    if (span > 0) {
+        const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst);
+        for (int r = 0; r < nranks; ++r) {
+            const uintptr_t s0 = reinterpret_cast<uintptr_t>(srcs[r]);
+            if (s0 == d0) continue;
+            if (s0 < d0 + (uintptr_t)span && d0 < s0 + (uintptr_t)span) return PTORED_ERR_OVERLAP;
+        }
+    }
+    return PTORED_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Choose the kernel family and the slot geometry ([TREDUCE] §4.1 analog).
+int make_plan(const void* const* srcs, int nranks, int root, const void* dst, int64_t rows,
+              int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols, int dtype,
+              int op, const ptored_tuning* tuning, Plan& p) {
+    (void)root;
+    const int st = validate(srcs, nranks, root, dst, rows, cols, ld, valid_rows, valid_cols,
+                            dtype, op);
+    if (st != PTORED_OK) return st;
+    const uint32_t flags = tuning ? tuning->flags : 0u;
+    p = Plan{};
+    p.dtype = dtype;
+    p.op = op;
+    p.nranks = nranks;
+    p.esize = esize_of(dtype);
+    p.valid_rows = valid_rows;
+    p.valid_cols = valid_cols;
+    p.ld = ld;
+    p.nt_loads = (flags & PTORED_NT_LOADS) != 0;
+    p.xcd_remap = (flags & PTORED_NO_XCD_REMAP) == 0;
+    p.blocks_per_cu = tuning ? tuning->blocks_per_cu : 0;
+    int64_t mlb = (tuning && tuning->max_launch_bytes > 0) ? tuning->max_launch_bytes
+                                                           : kDefaultLaunchBytes;
+    mlb = std::min<int64_t>(mlb, kDefaultLaunchBytes);
+    mlb = std::max<int64_t>(mlb & ~int64_t(15), 16);
+    p.max_launch_bytes = mlb;
+
+    if (valid_rows == 0 || valid_cols == 0) {
+        p.family = kFamNone;
+        p.launches = 0;
+        return PTORED_OK;
+    }
+    // One contiguous span when the valid rows follow each other with no gap.
+    const bool contiguous =
+        (valid_cols == ld || valid_rows == 1) && (flags & PTORED_FORCE_ROWS) == 0;
+    p.rows_mode = contiguous ? 0 : 1;
+    p.total_elems = contiguous ? (valid_rows == 1 ? valid_cols : valid_rows * ld) : 0;
+
+    bool use_vec = (flags & PTORED_FORCE_ELEMENTWISE) == 0 && aligned16(dst);
+    for (int r = 0; r < nranks && use_vec; ++r) use_vec = aligned16(srcs[r]);
+    if (use_vec && p.rows_mode && ((ld * p.esize) & 15) != 0) use_vec = false;
+
+    if (use_vec) {
+        p.vec_elems = 16 / p.esize;
+        if (nranks == 1) {
+            p.family = kFamCopy;
+            p.unroll = unroll_for(1);
+        } else if (nranks <= 16 && (flags & PTORED_FORCE_RUNTIME_N) == 0) {
+            p.family = kFamVecFixed;
+            p.unroll = unroll_for(nranks);
+        } else {
+            p.family = kFamVecRuntime;
+            p.unroll = kRuntimeUnroll;
+        }
+    } else {
+        p.family = kFamElem;
+        p.vec_elems = 1;
+        p.unroll = kElemUnroll;
+    }
+    const int64_t vec = p.vec_elems;
+    if (p.rows_mode) {
+        p.slots = valid_rows * ((valid_cols + vec - 1) / vec);
+    } else {
+        p.slots = (p.total_elems + vec - 1) / vec;
+    }
+    // Count launches (the same bands run() walks).
+    int64_t launches = 0;
+    const int64_t es = p.esize;
+    if (!p.rows_mode) {
+        const int64_t per = p.max_launch_bytes / es;
+        launches = (p.total_elems + per - 1) / per;
+    } else if (valid_cols * es <= p.max_launch_bytes) {
+        const int64_t ldb = ld * es;
+        const int64_t rpl = (p.max_launch_bytes - valid_cols * es) / ldb + 1;
+        launches = (valid_rows + rpl - 1) / rpl;
+    } else {
+        const int64_t per = p.max_launch_bytes / es;
+        launches = valid_rows * ((valid_cols + per - 1) / per);
+    }
+    p.launches = launches;
+    return PTORED_OK;
+}
+
+// Granlund-Montgomery multiplier for division by d >= 1 (32-bit dividends).
+FastDiv fast_div_for(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    FastDiv f;
+    f.mul = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+    f.sh1 = l < 1 ? l : 1;
+    f.sh2 = l > 1 ? l - 1 : 0;
+    return f;
+}
+
+int launch_one(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
+    switch (p.dtype) {
+    case PTORED_F32: return launch_f32(p, a, cu, s);
+    case PTORED_BF16: return launch_bf16(p, a, cu, s);
+    case PTORED_F16: return launch_f16(p, a, cu, s);
+    default: return launch_i32(p, a, cu, s);
+    }
+}
+
+// One launch over a contiguous run of `elems` elements starting at byte
+// offset `byte_off` of every buffer.
+int launch_span(const Plan& p, KArgs a, const char* const* ordered, char* dst, int64_t byte_off,
+                int64_t elems, int cu, hipStream_t s) {
+    const int64_t vec = p.vec_elems;
+    for (int r = 0; r < p.nranks; ++r) a.src[r] = ordered[r] + byte_off;
+    a.dst = dst + byte_off;
+    a.nslots = (uint32_t)((elems + vec - 1) / vec);
+    a.tail = (uint32_t)(elems - (int64_t)(a.nslots - 1) * vec);
+    a.nvec_row = a.nslots;
+    a.ld_bytes = 0;
+    a.div_row = fast_div_for(a.nslots);
+    const int64_t per_tile = (int64_t)256 * p.unroll;
+    a.ntiles = (uint32_t)((a.nslots + per_tile - 1) / per_tile);
+    Plan q = p;
+    q.rows_mode = 0;
+    return launch_one(q, a, cu, s);
+}
+
+// One launch over `nrows` rows of the valid rectangle starting at row `row0`.
+int launch_rows(const Plan& p, KArgs a, const char* const* ordered, char* dst, int64_t row0,
+                int64_t nrows, int cu, hipStream_t s) {
+    const int64_t vec = p.vec_elems;
+    const int64_t byte_off = row0 * p.ld * p.esize;
+    for (int r = 0; r < p.nranks; ++r) a.src[r] = ordered[r] + byte_off;
+    a.dst = dst + byte_off;
+    const int64_t per_row = (p.valid_cols + vec - 1) / vec;
+    a.nvec_row = (uint32_t)per_row;
+    a.tail = (uint32_t)(p.valid_cols - (per_row - 1) * vec);
+    a.nslots = (uint32_t)(per_row * nrows);
+    a.ld_bytes = nrows > 1 ? (uint32_t)(p.ld * p.esize) : 0u;
+    a.div_row = fast_div_for(a.nvec_row);
+    const int64_t per_tile = (int64_t)256 * p.unroll;
+    a.ntiles = (uint32_t)((a.nslots + per_tile - 1) / per_tile);
+    return launch_one(p, a, cu, s);
+}
+
+std::atomic<int> g_cu_cache[256];
+
+int cu_count_of_current_device(int& cu) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PTORED_ERR_HIP;
+    if (dev >= 0 && dev < 256) {
+        const int cached = g_cu_cache[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            cu = cached;
+            return PTORED_OK;
+        }
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+        return PTORED_ERR_HIP;
+    if (dev >= 0 && dev < 256) g_cu_cache[dev].store(n, std::memory_order_relaxed);
+    cu = n;
+    return PTORED_OK;
+}
+
+int run(const Plan& p, const void* const* srcs, int root, void* dst, hipStream_t stream) {
+    if (p.family == kFamNone) return PTORED_OK;
+    // Fold order of [TREDUCE] §4.3: the root's buffer first, then every
+    // other rank in ascending order.
+    const char* ordered[PTORED_MAX_RANKS];
+    ordered[0] = static_cast<const char*>(srcs[root]);
+    int k = 1;
+    for (int r = 0; r < p.nranks; ++r)
+        if (r != root) ordered[k++] = static_cast<const char*>(srcs[r]);
+
+    int cu = 0;
+    int st = cu_count_of_current_device(cu);
+    if (st != PTORED_OK) return st;
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+
+    KArgs a{};
+    a.nranks = (uint32_t)p.nranks;
+    a.xcd_remap = p.xcd_remap ? 1u : 0u;
+    char* d = static_cast<char*>(dst);
+    const int64_t es = p.esize;
+    int rc = 0;
+    if (!p.rows_mode) {
+        // One contiguous span, cut into launches of at most max_launch_bytes.
+        const int64_t per = p.max_launch_bytes / es;
+        for (int64_t e0 = 0; e0 < p.total_elems && rc == 0; e0 += per)
+            rc = launch_span(p, a, ordered, d, e0 * es, std::min(per, p.total_elems - e0), cu,
+                             stream);
+    } else if (p.valid_cols * es <= p.max_launch_bytes) {
+        // Row bands whose byte extent fits in 32-bit offsets.
+        const int64_t ldb = p.ld * es;
+        const int64_t rpl = (p.max_launch_bytes - p.valid_cols * es) / ldb + 1;
+        for (int64_t r0 = 0; r0 < p.valid_rows && rc == 0; r0 += rpl)
+            rc = launch_rows(p, a, ordered, d, r0, std::min(rpl, p.valid_rows - r0), cu, stream);
+    } else {
+        // Rows longer than one launch: every row is a contiguous span.
+        const int64_t per = p.max_launch_bytes / es;
+        for (int64_t r = 0; r < p.valid_rows && rc == 0; ++r)
+            for (int64_t c0 = 0; c0 < p.valid_cols && rc == 0; c0 += per)
+                rc = launch_span(p, a, ordered, d, (r * p.ld + c0) * es,
+                                 std::min(per, p.valid_cols - c0), cu, stream);
+    }
+    if (rc != 0) return PTORED_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return PTORED_ERR_HIP;
+    return PTORED_OK;
+}
+
+}  // namespace
+}  // namespace ptored
+
+using namespace ptored;
+
+extern "C" int ptored_treduce_ex(const void* const* srcs, int nranks, int root, void* dst,
+                                 int64_t rows, int64_t cols, int64_t ld, int64_t valid_rows,
+                                 int64_t valid_cols, int dtype, int op,
+                                 const ptored_tuning* tuning, hipStream_t stream) {
+    Plan p;
+    const int st = make_plan(srcs, nranks, root, dst, rows, cols, ld, valid_rows, valid_cols,
+                             dtype, op, tuning, p);
+    if (st != PTORED_OK) return st;
+    return run(p, srcs, root, dst, stream);
+}
+
+extern "C" int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst,
+                              int64_t rows, int64_t cols, int64_t ld, int64_t valid_rows,
+                              int64_t valid_cols, int dtype, int op, hipStream_t stream) {
+    return ptored_treduce_ex(srcs, nranks, root, dst, rows, cols, ld, valid_rows, valid_cols,
+                             dtype, op, nullptr, stream);
+}
+
+extern "C" int ptored_treduce_plan(const void* const* srcs, int nranks, int root,
+                                   const void* dst, int64_t rows, int64_t cols, int64_t ld,
+                                   int64_t valid_rows, int64_t valid_cols, int dtype, int op,
+                                   const ptored_tuning* tuning, ptored_plan_info* info) {
+    Plan p;
+    const int st = make_plan(srcs, nranks, root, dst, rows, cols, ld, valid_rows, valid_cols,
+                             dtype, op, tuning, p);
+    if (st != PTORED_OK) return st;
+    if (info) {
+        info->path = p.family;
+        info->rows_mode = p.rows_mode;
+        info->vec_elems = p.vec_elems;
+        info->slots_per_thread = p.unroll;
+        info->slots = p.slots;
+        info->launches = p.launches;
+    }
+    return PTORED_OK;
+}
+
+extern "C" const char* ptored_status_string(int status) {
+    switch (status) {
+    case PTORED_OK: return "PTORED_OK";
+    case PTORED_ERR_INVALID_ARG: return "PTORED_ERR_INVALID_ARG: bad rank count, root, pointer or shape";
+    case PTORED_ERR_UNSUPPORTED: return "PTORED_ERR_UNSUPPORTED: unknown dtype or op";
+    case PTORED_ERR_OVERLAP: return "PTORED_ERR_OVERLAP: dst partially overlaps a source";
+    case PTORED_ERR_HIP: return "PTORED_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown ptored status";
+    }
+}
+
+extern "C" int ptored_abi_version(void) { return PTORED_ABI_VERSION; }
+
+extern "C" int ptored_max_ranks(void) { return PTORED_MAX_RANKS; }

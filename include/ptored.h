@@ -1,0 +1,169 @@
+/*
+ * ptored.h -- C ABI of the N-way cross-rank reduction on one MI355X (gfx950).
+ *
+ * Sources (cited by title and section):
+ *   [TREDUCE]  "CANN PTO-ISA TREDUCE instruction explained: principle,
+ *              constraints and practice of multi-NPU cross-card Reduce"
+ *              (lpnh.cn news article on pto-isa).
+ *   [N6]       "Distributed Operators (N6)", PyPTO developer documentation.
+ *
+ * The operation ([TREDUCE] §1.1): for every element (i, j) of a valid
+ * rectangle, dst[i, j] = src_0[i, j] (+) src_1[i, j] (+) ... (+) src_{N-1}[i, j].
+ * The N sources are the N ranks' window slices ([N6] overview); on one GPU
+ * they are N separate device buffers.  The fold starts from the root's value
+ * and then takes every other rank in ascending order ([TREDUCE] §4.3), and
+ * every step rounds to the element type (the accumulator tile has the element
+ * type, [TREDUCE] §1.3 and §3.1).
+ *
+ * Layout shared by every buffer (all sources and dst have the same shape and
+ * strides, [TREDUCE] §3.3): row-major, `rows` rows of `ld` elements, of which
+ * the first `cols` are the tensor's columns; element (i, j) is at element
+ * offset i*ld + j.  The valid rectangle [0, valid_rows) x [0, valid_cols) is
+ * anchored at (0, 0) ([N6] pld.tensor.allreduce, valid_shape).  A buffer must
+ * hold at least ((rows-1)*ld + cols) elements.
+ *
+ * All values of the enums are append-only: new values are only ever added at
+ * the end, so an integer keeps its meaning ([N6] "ABI enums").
+ *
+ * All functions are thread-safe.  No function allocates device memory; the
+ * library keeps no state besides a per-device cache of the compute-unit count.
+ */
+#ifndef PTORED_H
+#define PTORED_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PTORED_ABI_VERSION 1
+/* Largest number of ranks (source buffers) one call accepts. */
+#define PTORED_MAX_RANKS 64
+
+/* Element type.  One type for every source and for dst ([TREDUCE] §3.1). */
+typedef enum ptored_dtype {
+    PTORED_F32 = 0,  /* IEEE binary32 */
+    PTORED_BF16 = 1, /* bfloat16 (upper half of a binary32) */
+    PTORED_F16 = 2,  /* IEEE binary16 */
+    PTORED_I32 = 3   /* two's-complement int32 */
+} ptored_dtype;
+
+/* Reduction ([TREDUCE] §1.3 ReduceOp; [N6] ReduceOp enum, same values).
+ *   SUM  float: exact sum rounded to the element type (nearest, ties to
+ *        even, subnormals kept); i32: wraps modulo 2^32.
+ *   MAX / MIN  i32: signed.  float: a NaN operand gives NaN; otherwise the
+ *        extremum with -0 ordered below +0 (IEEE-754 maximum / minimum).
+ *   PROD float: exact product rounded to the element type; i32: wraps. */
+typedef enum ptored_op {
+    PTORED_SUM = 0,
+    PTORED_MAX = 1,
+    PTORED_MIN = 2,
+    PTORED_PROD = 3
+} ptored_op;
+
+/* Status codes; every function returns one of these (never throws). */
+typedef enum ptored_status {
+    PTORED_OK = 0,
+    PTORED_ERR_INVALID_ARG = -1, /* bad count, root, pointer or shape */
+    PTORED_ERR_UNSUPPORTED = -2, /* unknown dtype or op */
+    PTORED_ERR_OVERLAP = -3,     /* dst partially overlaps a source */
+    PTORED_ERR_HIP = -4          /* the HIP runtime reported an error */
+} ptored_status;
+
+/*
+ * ptored_treduce -- dst = fold of the N sources over the valid rectangle.
+ *
+ * srcs        HOST array of `nranks` DEVICE pointers; srcs[r] is rank r's
+ *             buffer.  The array is read during the call only and may be
+ *             freed when the call returns.
+ * nranks      N, 1 <= N <= PTORED_MAX_RANKS ([TREDUCE] §3.3: group size > 0).
+ * root        0 <= root < N ([TREDUCE] §3.3).  The fold starts from the
+ *             root's value (the root's buffer is the reference, §3.3 and
+ *             §4.3); with N == 1 the call is a bitwise copy (§4.3).
+ * dst         DEVICE pointer to the output buffer.  Only elements inside the
+ *             valid rectangle are written; dst is never read, and every
+ *             other byte is left unchanged.  dst may be exactly one of the
+ *             sources (in-place, as the allreduce of [N6] does); any other
+ *             overlap of dst with a source's span is rejected.
+ * rows, cols, ld              buffer shape (elements), cols <= ld.
+ * valid_rows, valid_cols      valid rectangle, <= rows and <= cols.  An empty
+ *             rectangle returns PTORED_OK and launches nothing ([TREDUCE]
+ *             §4.1 empty short-circuit).
+ * dtype, op   ptored_dtype and ptored_op values.
+ * stream      HIP stream of the current device (0 = null stream).  The call
+ *             only enqueues work and returns; it never synchronises.  Every
+ *             buffer must stay valid and unmodified until that work is done
+ *             ([TREDUCE] §3.2).
+ *
+ * Errors are checked before any HIP call, in this order: INVALID_ARG (N or
+ * root out of range, a null pointer, a negative size, cols > ld,
+ * valid_rows > rows, valid_cols > cols, a size whose byte extent overflows),
+ * UNSUPPORTED (dtype or op outside the enums), OVERLAP.  ERR_HIP is returned
+ * when the launch fails.  Misaligned pointers or strides are not errors:
+ * they select an element-wise kernel.
+ */
+int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int64_t rows,
+                   int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
+                   int dtype, int op, hipStream_t stream);
+
+/* Forcing flags of ptored_treduce_ex (for tests and tuning; 0 = automatic). */
+#define PTORED_FORCE_ELEMENTWISE 0x1u /* element-wise kernel even when 16-B aligned */
+#define PTORED_FORCE_ROWS 0x2u        /* 2-D row walk even for a contiguous region */
+#define PTORED_FORCE_RUNTIME_N 0x4u   /* rank-count loop instead of an unrolled N */
+#define PTORED_NO_XCD_REMAP 0x8u      /* plain block order instead of per-XCD ranges */
+#define PTORED_NT_LOADS 0x10u         /* non-temporal source loads */
+
+/* Launch choices of ptored_treduce_ex. */
+typedef struct ptored_tuning {
+    uint32_t flags;         /* PTORED_FORCE_* / PTORED_NO_XCD_REMAP / PTORED_NT_LOADS */
+    int32_t blocks_per_cu;  /* workgroups per compute unit in the persistent grid; 0 = auto */
+    int64_t max_launch_bytes; /* split a call into launches of at most this many bytes of
+                                 row span per buffer; 0 = auto (2^31) */
+} ptored_tuning;
+
+/* ptored_treduce with explicit launch choices; `tuning` may be NULL (= all
+ * automatic).  Results are identical for every choice. */
+int ptored_treduce_ex(const void* const* srcs, int nranks, int root, void* dst, int64_t rows,
+                      int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
+                      int dtype, int op, const ptored_tuning* tuning, hipStream_t stream);
+
+/* Kernel family the automatic choice would take (no HIP call, no launch). */
+#define PTORED_PATH_NONE 0        /* empty rectangle: nothing launched */
+#define PTORED_PATH_COPY 1        /* N == 1 copy */
+#define PTORED_PATH_VEC_FIXED 2   /* 16-B vectors, N unrolled at compile time */
+#define PTORED_PATH_VEC_RUNTIME 3 /* 16-B vectors, rank-count loop */
+#define PTORED_PATH_ELEMENTWISE 4 /* one element per slot (misaligned data) */
+
+typedef struct ptored_plan_info {
+    int32_t path;          /* PTORED_PATH_* */
+    int32_t rows_mode;     /* 1: 2-D row walk; 0: one contiguous span */
+    int32_t vec_elems;     /* elements per slot */
+    int32_t slots_per_thread; /* slots one thread handles per tile */
+    int64_t slots;         /* slots in the whole call */
+    int64_t launches;      /* kernel launches the call is split into */
+} ptored_plan_info;
+
+/* Validate like ptored_treduce_ex and describe the launch it would make,
+ * without any HIP call.  Returns the same status codes. */
+int ptored_treduce_plan(const void* const* srcs, int nranks, int root, const void* dst,
+                        int64_t rows, int64_t cols, int64_t ld, int64_t valid_rows,
+                        int64_t valid_cols, int dtype, int op, const ptored_tuning* tuning,
+                        ptored_plan_info* info);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* ptored_status_string(int status);
+
+/* PTORED_ABI_VERSION of the built library. */
+int ptored_abi_version(void);
+
+/* PTORED_MAX_RANKS of the built library. */
+int ptored_max_ranks(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTORED_H */

@@ -1,0 +1,164 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, maps one HIP runtime, and returns every error status (and the empty
+short-circuit) before it makes any HIP call."""
+
+import os
+import re
+
+import pytest
+
+import cross_rank_collective_amd as crc
+from cross_rank_collective_amd import binding as B
+from cross_rank_collective_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Fake device addresses: never dereferenced, because every call below stops
+# in the host-side checks or the empty short-circuit.
+A = [0x10000000 + 0x1000000 * r for r in range(80)]
+D = 0x7F000000
+
+
+def _header_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ptored_\w+)\s*\(", text,
+                                    flags=re.M))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = _header_functions()
+    for n in ("ptored_treduce", "ptored_treduce_ex", "ptored_treduce_plan",
+              "ptored_status_string", "ptored_abi_version", "ptored_max_ranks"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    for name in _header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_one_hip_runtime_is_mapped():
+    B.load()
+    maps = open("/proc/self/maps").read().splitlines()
+    paths = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    assert len(paths) == 1, paths
+
+
+def test_version_and_limits():
+    assert crc.ptored_abi_version() == 1
+    assert crc.ptored_max_ranks() == 64
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        s = crc.ptored_status_string(st)
+        assert s.startswith("PTORED_")
+    assert "unknown" in crc.ptored_status_string(7)
+
+
+def _call(n=2, root=0, dst=D, rows=4, cols=4, ld=4, vr=4, vc=4, dtype=0, op=0, srcs=None):
+    srcs = A[:n] if srcs is None else srcs
+    return crc.ptored_treduce(srcs, n, root, dst, rows, cols, ld, vr, vc, dtype, op, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), -1), (dict(n=65), -1), (dict(root=2), -1), (dict(root=-1), -1),
+    (dict(dst=0), -1), (dict(srcs=[A[0], 0]), -1), (dict(rows=-1), -1), (dict(cols=-1), -1),
+    (dict(ld=-1), -1), (dict(vr=-1), -1), (dict(vc=-1), -1), (dict(cols=5), -1),
+    (dict(vr=5), -1), (dict(vc=5, cols=4, ld=8), -1), (dict(rows=1 << 40, ld=1 << 30), -1),
+    (dict(dtype=4), -2), (dict(dtype=-1), -2), (dict(op=4), -2), (dict(op=-1), -2),
+    (dict(dst=A[1] + 4), -3), (dict(dst=A[0] - 8), -3),
+])
+def test_argument_errors_before_any_hip_call(kw, status):
+    assert _call(**kw) == status
+
+
+def test_invalid_beats_unsupported_beats_overlap():
+    assert _call(root=9, dtype=9) == -1
+    assert _call(dtype=9, dst=A[1] + 4) == -2
+
+
+def test_empty_region_returns_ok_without_launch():
+    assert _call(vr=0) == 0
+    assert _call(vc=0) == 0
+    assert _call(rows=0, vr=0) == 0
+    assert _call(n=64, srcs=A[:64], vr=0, dtype=2, op=3) == 0
+
+
+def _plan(n=2, root=0, dst=D, rows=4, cols=4, ld=4, vr=4, vc=4, dtype=0, op=0, srcs=None,
+          tuning=None):
+    srcs = A[:n] if srcs is None else srcs
+    st, info = crc.ptored_treduce_plan(srcs, n, root, dst, rows, cols, ld, vr, vc, dtype, op,
+                                       tuning)
+    assert st == 0
+    return info
+
+
+def test_exact_alias_is_allowed_in_place():
+    info = _plan(n=3, dst=A[1])
+    assert B.PATHS[info.path] == "vec_fixed"
+
+
+def test_plan_paths():
+    assert B.PATHS[_plan(vr=0).path] == "none"
+    assert B.PATHS[_plan(n=1).path] == "copy"
+    assert B.PATHS[_plan(n=16, srcs=A[:16]).path] == "vec_fixed"
+    assert B.PATHS[_plan(n=17, srcs=A[:17]).path] == "vec_runtime"
+    assert B.PATHS[_plan(n=64, srcs=A[:64]).path] == "vec_runtime"
+    # a misaligned source pointer or row pitch selects the element-wise kernel
+    assert B.PATHS[_plan(srcs=[A[0], A[1] + 4]).path] == "elementwise"
+    assert B.PATHS[_plan(dst=D + 2, dtype=2).path] == "elementwise"
+    assert B.PATHS[_plan(rows=4, cols=3, ld=5, vr=4, vc=3).path] == "elementwise"
+    # forcing flags
+    t = B.tuning(flags=B.PTORED_FORCE_ELEMENTWISE)
+    assert B.PATHS[_plan(tuning=t).path] == "elementwise"
+    t = B.tuning(flags=B.PTORED_FORCE_RUNTIME_N)
+    assert B.PATHS[_plan(tuning=t).path] == "vec_runtime"
+
+
+def test_plan_walk_and_slots():
+    info = _plan(rows=8, cols=8, ld=8, vr=8, vc=8)  # contiguous f32
+    assert (info.rows_mode, info.vec_elems, info.slots, info.launches) == (0, 4, 16, 1)
+    info = _plan(rows=8, cols=10, ld=12, vr=7, vc=10)  # 2-D: 3 slots per row
+    assert (info.rows_mode, info.slots) == (1, 21)
+    info = _plan(rows=8, cols=8, ld=8, vr=8, vc=8, tuning=B.tuning(flags=B.PTORED_FORCE_ROWS))
+    assert (info.rows_mode, info.slots) == (1, 16)
+    info = _plan(rows=1, cols=13, ld=16, vr=1, vc=13, dtype=2)  # one row: contiguous f16
+    assert (info.rows_mode, info.vec_elems, info.slots) == (0, 8, 2)
+
+
+def test_plan_launch_split():
+    # contiguous: 4096 f32 = 16 KiB in launches of 4 KiB
+    info = _plan(rows=64, cols=64, ld=64, vr=64, vc=64, tuning=B.tuning(max_launch_bytes=4096))
+    assert info.launches == 4
+    # rows: 10 rows, pitch 64 B, 40 valid bytes per row, 256-byte launches:
+    # (256 - 40) // 64 + 1 = 4 rows per launch -> 3 launches
+    info = _plan(rows=10, cols=10, ld=16, vr=10, vc=10, tuning=B.tuning(max_launch_bytes=256))
+    assert (info.rows_mode, info.launches) == (1, 3)
+    # rows longer than one launch: every row is split into spans
+    info = _plan(rows=3, cols=100, ld=104, vr=3, vc=100, tuning=B.tuning(max_launch_bytes=128))
+    assert info.launches == 3 * 4
+
+
+def test_workload_plans():
+    """Each named workload takes the kernel family its shape calls for."""
+    want = {
+        "n2_f32_16x16": ("vec_fixed", 0),
+        "n4_f32_1024x1024_valid1000x1000": ("vec_fixed", 1),
+        "n8_bf16_8192x8192": ("vec_fixed", 0),
+        "n16_i32_4096x4096": ("vec_fixed", 0),
+        "n8_f16_8192x12288_valid8191x12287": ("vec_fixed", 1),
+    }
+    for name, w in W.WORKLOADS.items():
+        info = _plan(n=w.nranks, srcs=A[:w.nranks], rows=w.rows, cols=w.cols, ld=w.ld,
+                     vr=w.valid_rows, vc=w.valid_cols, dtype=B.DTYPES[w.dtype],
+                     op=B.OPS[w.ops[0]])
+        assert (B.PATHS[info.path], info.rows_mode) == want[name], name
+        assert info.launches == 1

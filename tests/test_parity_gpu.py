@@ -1,0 +1,314 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: bit-exact for every dtype and op (i32; Max/Min; float Sum/Prod in the
+fold order root-first-then-ascending, which the kernels keep), NaN compared
+by NaN-ness.  Cells outside the valid rectangle and the guard bands around
+dst keep their sentinel bytes; sources are never written.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from cross_rank_collective_amd import binding as B
+from cross_rank_collective_amd import workloads as W
+from tests.gpu_helpers import (compare, oracle_reduce, run_gpu, say, sentinel, valid_mask,
+                               DevBuf, ESIZE, STORAGE)
+
+pytestmark = pytest.mark.gpu
+
+DT = ["f32", "bf16", "f16", "i32"]
+OPS = ["sum", "max", "min", "prod"]
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+
+
+def _rand_elems(dtype, rng, n, wild=0.15):
+    """Values of the kind the reduction meets, with a share of arbitrary bit
+    patterns (NaN, Inf, subnormals, signed zeros) mixed in."""
+    if dtype == "i32":
+        v = rng.integers(-2**31, 2**31, n, dtype=np.int64)
+        small = rng.integers(-1000, 1000, n)
+        return np.where(rng.random(n) < 0.5, small, v).astype(np.int32)
+    g = rng.standard_normal(n).astype(np.float32) * np.exp2(rng.integers(-8, 8, n)).astype(
+        np.float32)
+    if dtype == "f32":
+        raw = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        out = np.where(rng.random(n) < wild, raw, g).astype(np.float32)
+        out[rng.random(n) < 0.02] = 0.0
+        out[rng.random(n) < 0.02] = -0.0
+        return out
+    if dtype == "f16":
+        soft = g.astype(np.float16).view(np.uint16)
+    else:
+        soft = torch.from_numpy(g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    raw = rng.integers(0, 65536, n).astype(np.uint16)
+    out = np.where(rng.random(n) < wild, raw, soft).astype(np.uint16)
+    out[rng.random(n) < 0.02] = 0x0000
+    out[rng.random(n) < 0.02] = 0x8000
+    return out
+
+
+def _check(srcs, dtype, op, root, rows, cols, ld, vr, vc, dst, bufs, alias=-1, label=""):
+    size = (rows - 1) * ld + cols if rows > 0 else 0
+    got = dst.download(dtype)
+    want = oracle_reduce(srcs, dtype, op, root, rows, cols, ld, vr, vc,
+                         lambda n: sentinel(dtype, n) if alias < 0 else srcs[alias][:n].copy())
+    m = valid_mask(rows, ld, vr, vc, max(size, 1)) if size else np.zeros(1, bool)
+    ok = compare(dtype, got, want)
+    bad = np.flatnonzero(~ok & m)
+    assert bad.size == 0, (label, bad[:8], got[bad[:4]], want[bad[:4]])
+    # outside the valid rectangle: untouched bytes
+    outside = ~m
+    if alias < 0:
+        assert np.array_equal(got.view(np.uint8).reshape(-1, ESIZE[dtype])[outside],
+                              np.full((outside.sum(), ESIZE[dtype]), 0xFF, np.uint8)), label
+    else:
+        assert np.array_equal(got[outside].view(np.uint8),
+                              srcs[alias][:max(size, 1)][outside].view(np.uint8)), label
+    assert dst.guards_intact(), label
+    for r, b in enumerate(bufs):
+        if r != alias:
+            assert np.array_equal(b.download(dtype).view(np.uint8),
+                                  srcs[r][:max(size, 1)].view(np.uint8)), (label, "src", r)
+
+
+VARIANTS = [
+    ("auto", 0, 0),
+    ("elementwise", B.PTORED_FORCE_ELEMENTWISE, 0),
+    ("rows", B.PTORED_FORCE_ROWS, 0),
+    ("runtime_n", B.PTORED_FORCE_RUNTIME_N, 0),
+    ("nt_noremap", B.PTORED_NT_LOADS | B.PTORED_NO_XCD_REMAP, 0),
+    ("one_block_per_cu", 0, 1),
+    ("block_per_tile", 0, -1),
+]
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_random_small_cases(dtype):
+    """Tiny shapes, every op, N from 1 to 64, any root, odd pitches, misaligned
+    pointers, sub-rectangles and every kernel variant."""
+    rng = np.random.default_rng({"f32": 11, "bf16": 12, "f16": 13, "i32": 14}[dtype])
+    es = ESIZE[dtype]
+    for case in range(40):
+        n = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 17, 33, 64]))
+        rows = int(rng.integers(1, 9))
+        cols = int(rng.integers(1, 80))
+        ld = cols + int(rng.choice([0, 0, 1, 3, 8, 16]))
+        vr = int(rng.integers(1, rows + 1))
+        vc = int(rng.integers(1, cols + 1))
+        root = int(rng.choice([0, n - 1, int(rng.integers(0, n))]))
+        op = OPS[case % 4]
+        vname, flags, bpc = VARIANTS[case % len(VARIANTS)]
+        aligned = rng.random() < 0.6
+        offs = [0 if aligned else int(rng.integers(0, 8)) * es for _ in range(n)]
+        dst_off = 0 if aligned else int(rng.integers(0, 8)) * es
+        size = (rows - 1) * ld + cols
+        srcs = [_rand_elems(dtype, rng, size) for _ in range(n)]
+        t = B.tuning(flags=flags, blocks_per_cu=bpc)
+        label = f"small#{case} {vname}"
+        dst, st, bufs = run_gpu(srcs, dtype, op, root, rows, cols, ld, vr, vc, offsets=offs,
+                                dst_offset=dst_off, tuning=t, label=label)
+        assert st == 0, B.ptored_status_string(st)
+        _check(srcs, dtype, op, root, rows, cols, ld, vr, vc, dst, bufs, label=label)
+
+
+MEDIUM = [
+    # rows, cols, ld, valid_rows, valid_cols
+    (129, 1000, 1024, 129, 999),
+    (3, 70001, 70008, 3, 70001),
+    (64, 512, 512, 64, 512),
+    (1, 200003, 200003, 1, 200003),
+    (257, 333, 336, 250, 331),
+]
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_medium_cases_span_many_tiles(dtype):
+    """Shapes that span many tiles and several grid-stride passes, with ragged
+    row ends, one very long row and sub-rectangles."""
+    rng = np.random.default_rng({"f32": 21, "bf16": 22, "f16": 23, "i32": 24}[dtype])
+    for case, (rows, cols, ld, vr, vc) in enumerate(MEDIUM):
+        for n, op, vname, flags, bpc in [(4, OPS[case % 4], "auto", 0, 1),
+                                         (9, OPS[(case + 1) % 4], "rows", B.PTORED_FORCE_ROWS, 0),
+                                         (16, OPS[(case + 2) % 4], "auto", 0, 0),
+                                         (20, OPS[(case + 3) % 4], "runtime_n", 0, 0),
+                                         (3, OPS[case % 4], "elementwise",
+                                          B.PTORED_FORCE_ELEMENTWISE, 2)]:
+            size = (rows - 1) * ld + cols
+            srcs = [_rand_elems(dtype, rng, size, wild=0.02) for _ in range(n)]
+            root = int(rng.integers(0, n))
+            t = B.tuning(flags=flags, blocks_per_cu=bpc)
+            label = f"medium#{case} N={n} {vname}"
+            dst, st, bufs = run_gpu(srcs, dtype, op, root, rows, cols, ld, vr, vc, tuning=t,
+                                    label=label)
+            assert st == 0
+            _check(srcs, dtype, op, root, rows, cols, ld, vr, vc, dst, bufs, label=label)
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_split_into_many_launches(dtype):
+    """A tiny launch byte limit splits one call into many launches: contiguous
+    spans, row bands, and rows cut into spans."""
+    rng = np.random.default_rng(31)
+    es = ESIZE[dtype]
+    for rows, cols, ld, vr, vc, mlb in [(40, 256, 256, 40, 256, 1024),
+                                        (40, 250, 264, 37, 249, 3000),
+                                        (5, 3000, 3008, 5, 2999, 512)]:
+        n = 5
+        size = (rows - 1) * ld + cols
+        srcs = [_rand_elems(dtype, rng, size, wild=0.02) for _ in range(n)]
+        for flags in (0, B.PTORED_FORCE_ELEMENTWISE):
+            t = B.tuning(flags=flags, max_launch_bytes=mlb)
+            st_plan, info = B.ptored_treduce_plan([0x100000] * n, n, 1, 0x900000, rows, cols, ld,
+                                                  vr, vc, B.DTYPES[dtype], 0, t)
+            assert st_plan == 0 and info.launches > 1
+            label = f"split mlb={mlb} launches={info.launches} flags={flags}"
+            dst, st, bufs = run_gpu(srcs, dtype, "sum", 1, rows, cols, ld, vr, vc, tuning=t,
+                                    label=label)
+            assert st == 0
+            _check(srcs, dtype, "sum", 1, rows, cols, ld, vr, vc, dst, bufs, label=label)
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_in_place_into_one_source(dtype):
+    """dst is exactly one of the sources (the allreduce's in-place store)."""
+    rng = np.random.default_rng(41)
+    rows, cols, ld, vr, vc = 33, 500, 512, 30, 497
+    size = (rows - 1) * ld + cols
+    for n, alias, op in [(4, 0, "sum"), (4, 2, "max"), (12, 11, "min"), (1, 0, "sum"),
+                         (20, 5, "sum")]:
+        srcs = [_rand_elems(dtype, rng, size, wild=0.02) for _ in range(n)]
+        dst, st, bufs = run_gpu(srcs, dtype, op, n // 2, rows, cols, ld, vr, vc, alias=alias,
+                                label=f"alias={alias}")
+        assert st == 0
+        _check(srcs, dtype, op, n // 2, rows, cols, ld, vr, vc, dst, bufs, alias=alias,
+               label=f"alias={alias}")
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_poison_outside_valid_never_reaches_output(dtype):
+    rng = np.random.default_rng(51)
+    rows, cols, ld, vr, vc, n = 20, 300, 304, 17, 293, 6
+    size = (rows - 1) * ld + cols
+    poison = {"f32": np.float32(np.nan), "i32": np.int32(-2**31), "bf16": np.uint16(0x7FC1),
+              "f16": np.uint16(0x7E01)}[dtype]
+    m = valid_mask(rows, ld, vr, vc, size)
+    clean = [_rand_elems(dtype, rng, size, wild=0.0) for _ in range(n)]
+    dirty = [np.where(m, s, poison).astype(s.dtype) for s in clean]
+    for op in OPS:
+        dst, st, bufs = run_gpu(dirty, dtype, op, 2, rows, cols, ld, vr, vc, label="poison")
+        assert st == 0
+        _check(dirty, dtype, op, 2, rows, cols, ld, vr, vc, dst, bufs, label="poison")
+        want = oracle_reduce(clean, dtype, op, 2, rows, cols, ld, vr, vc,
+                             lambda k: sentinel(dtype, k))
+        assert compare(dtype, dst.download(dtype)[m], want[m]).all()
+
+
+def test_rounding_edges_bf16_f16():
+    """Operand pairs around ties, overflow and subnormals for the 16-bit float
+    sums and products, every pattern against the oracle."""
+    rng = np.random.default_rng(61)
+    for dtype in ("bf16", "f16"):
+        base = np.arange(0, 65536, dtype=np.uint32)
+        near = (base + rng.integers(-4, 5, base.size)) & 0xFFFF
+        far = rng.integers(0, 65536, base.size)
+        a = np.concatenate([base, base]).astype(np.uint16)
+        b = np.concatenate([near, far]).astype(np.uint16)
+        for op in ("sum", "prod", "max", "min"):
+            dst, st, bufs = run_gpu([a, b], dtype, op, 0, 1, a.size, a.size, 1, a.size,
+                                    label="edges")
+            assert st == 0
+            _check([a, b], dtype, op, 0, 1, a.size, a.size, 1, a.size, dst, bufs,
+                   label=f"edges {dtype} {op}")
+
+
+def test_empty_region_launches_nothing_and_writes_nothing():
+    d = DevBuf(1024)
+    s = DevBuf(1024, fill=0)
+    for vr, vc in ((0, 16), (16, 0)):
+        st = B.ptored_treduce([s.ptr, s.ptr], 2, 0, d.ptr, 16, 16, 16, vr, vc, 0, 0,
+                              torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert st == 0
+        assert np.all(d.download_all() == 0xFF)
+
+
+def test_tensor_wrapper_and_side_stream():
+    torch.manual_seed(0)
+    xs = [torch.randn(300, 500, device="cuda") for _ in range(5)]
+    out = torch.empty(300, 500, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        from cross_rank_collective_amd import treduce
+        treduce(xs, out, op="max", root=3)
+    s.synchronize()
+    want = oracle_reduce([x.cpu().numpy().reshape(-1) for x in xs], "f32", "max", 3, 300, 500,
+                         500, 300, 500, lambda k: sentinel("f32", k))
+    assert np.array_equal(out.cpu().numpy().reshape(-1), want)
+    with pytest.raises(B.PtoredError):
+        treduce(xs, out, root=7)
+
+
+# -------------------------------------------------- full-size workloads ---
+
+def _workload_srcs(w):
+    say("generate", w.name)
+    return W.make_sources(w)
+
+
+def _sample_rows(w, rng, k=10):
+    rows = {0, 1, w.valid_rows - 2, w.valid_rows - 1}
+    rows.update(int(r) for r in rng.integers(0, w.valid_rows, k))
+    return sorted(r for r in rows if 0 <= r < w.valid_rows)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_workload_full_size(name):
+    """Each named workload at its full size, in the launch configuration the
+    benchmark uses.  Small workloads and the i32 one are compared in full;
+    the two large float ones on sampled rows (first, last, random), plus the
+    untouched-outside property over the whole buffer."""
+    w = W.WORKLOADS[name]
+    srcs = _workload_srcs(w)
+    rng = np.random.default_rng(7)
+    full_compare = w.dtype == "i32" or w.buffer_elems <= 1 << 21
+    variants = [("auto", 0)]
+    if w.valid_cols == w.ld:
+        variants.append(("rows", B.PTORED_FORCE_ROWS))  # the 2-D walk on the same data
+    es = w.esize
+    for op in w.ops:
+        results = []
+        for vname, flags in variants:
+            label = f"{name} {op} {vname}"
+            dst, st, bufs = run_gpu(srcs, w.dtype, op, w.root, w.rows, w.cols, w.ld,
+                                    w.valid_rows, w.valid_cols, tuning=B.tuning(flags=flags),
+                                    label=label)
+            assert st == 0
+            got = dst.download(w.dtype)
+            assert dst.guards_intact()
+            results.append(got)
+            del bufs
+            m = valid_mask(w.rows, w.ld, w.valid_rows, w.valid_cols, w.buffer_elems)
+            # untouched outside the valid rectangle, over the whole buffer
+            assert np.all(got.view(np.uint8).reshape(-1, es)[~m] == 0xFF), label
+            if full_compare:
+                want = oracle_reduce(srcs, w.dtype, op, w.root, w.rows, w.cols, w.ld,
+                                     w.valid_rows, w.valid_cols, lambda k: sentinel(w.dtype, k))
+                assert compare(w.dtype, got[m], want[m]).all(), label
+            else:
+                for r in _sample_rows(w, rng):
+                    lo = r * w.ld
+                    row_srcs = [s[lo:lo + w.cols] for s in srcs]
+                    want = oracle_reduce(row_srcs, w.dtype, op, w.root, 1, w.cols, w.cols, 1,
+                                         w.valid_cols, lambda k: sentinel(w.dtype, k))
+                    seg = got[lo:lo + w.valid_cols]
+                    assert compare(w.dtype, seg, want[:w.valid_cols]).all(), (label, r)
+        if len(results) > 1:
+            assert np.array_equal(results[0].view(np.uint8), results[1].view(np.uint8))
+        torch.cuda.empty_cache()
