@@ -48,6 +48,11 @@ int validate(const void* const* srcs, int nranks, int root, const void* dst, int
     if (rows > 0 && ld > 0 && rows > kMaxElems / ld) return PTORED_ERR_INVALID_ARG;
     if (dtype < PTORED_F32 || dtype > PTORED_I32) return PTORED_ERR_UNSUPPORTED;
     if (op < PTORED_SUM || op > PTORED_PROD) return PTORED_ERR_UNSUPPORTED;
+    // Every pointer holds whole elements (natural alignment of the type).
+    const uintptr_t amask = (uintptr_t)esize_of(dtype) - 1u;
+    if ((reinterpret_cast<uintptr_t>(dst) & amask) != 0) return PTORED_ERR_INVALID_ARG;
+    for (int r = 0; r < nranks; ++r)
+        if ((reinterpret_cast<uintptr_t>(srcs[r]) & amask) != 0) return PTORED_ERR_INVALID_ARG;
     // dst may be exactly a source (in place: each element is read by the one
     // thread that later writes it); any other overlap is a race.
     const int es = esize_of(dtype);
@@ -82,7 +87,6 @@ int make_plan(const void* const* srcs, int nranks, int root, const void* dst, in
     p.valid_rows = valid_rows;
     p.valid_cols = valid_cols;
     p.ld = ld;
-    p.nt_loads = (flags & PTORED_NT_LOADS) != 0;
     p.xcd_remap = (flags & PTORED_NO_XCD_REMAP) == 0;
     p.blocks_per_cu = tuning ? tuning->blocks_per_cu : 0;
     int64_t mlb = (tuning && tuning->max_launch_bytes > 0) ? tuning->max_launch_bytes
@@ -126,6 +130,20 @@ int make_plan(const void* const* srcs, int nranks, int root, const void* dst, in
     const int64_t vec = p.vec_elems;
     if (p.rows_mode) {
         p.slots = valid_rows * ((valid_cols + vec - 1) / vec);
+        // Default: the flattened walk.  On request, row tiles -- when a
+        // row's full slots fill its column chunks well (at least 7/8 of the
+        // threads busy, or 8+ chunks per row).  Row tiles keep every wave's
+        // 1 KiB run inside one row and cache-line aligned (no line is
+        // fetched twice), yet on MI355X the flattened walk measured faster
+        // on ragged rows, so it stays the default.
+        p.rows_mode = kWalkFlat;
+        if (p.family != kFamElem && (flags & PTORED_ROW_TILES) != 0) {
+            const int64_t full = valid_cols / vec;
+            const int64_t per_tile = (int64_t)kBlock * p.unroll;
+            const int64_t tiles = (full + per_tile - 1) / per_tile;
+            if (full > 0 && (full * 8 >= tiles * per_tile * 7 || tiles >= 8))
+                p.rows_mode = kWalkRowTiles;
+        }
     } else {
         p.slots = (p.total_elems + vec - 1) / vec;
     }
@@ -167,40 +185,90 @@ int launch_one(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
     }
 }
 
+void finish_tiles(const Plan& p, KArgs& a) {
+    const uint64_t per_main = (uint64_t)kBlock * p.unroll;
+    const uint64_t per_tail = (uint64_t)kBlock * (p.family == kFamElem ? kElemUnroll : 1);
+    a.main_tiles = (uint32_t)((a.nslots + per_main - 1) / per_main);
+    a.total_tiles = a.main_tiles + (uint32_t)((a.ntail + per_tail - 1) / per_tail);
+}
+
 // One launch over a contiguous run of `elems` elements starting at byte
-// offset `byte_off` of every buffer.
+// offset `byte_off` of every buffer: full 16-byte slots, then the remainder
+// (every element on the element-wise path).
 int launch_span(const Plan& p, KArgs a, const char* const* ordered, char* dst, int64_t byte_off,
                 int64_t elems, int cu, hipStream_t s) {
-    const int64_t vec = p.vec_elems;
     for (int r = 0; r < p.nranks; ++r) a.src[r] = ordered[r] + byte_off;
     a.dst = dst + byte_off;
-    a.nslots = (uint32_t)((elems + vec - 1) / vec);
-    a.tail = (uint32_t)(elems - (int64_t)(a.nslots - 1) * vec);
-    a.nvec_row = a.nslots;
+    a.extent = (uint32_t)(elems * p.esize);
     a.ld_bytes = 0;
-    a.div_row = fast_div_for(a.nslots);
-    const int64_t per_tile = (int64_t)256 * p.unroll;
-    a.ntiles = (uint32_t)((a.nslots + per_tile - 1) / per_tile);
+    a.div_slots = fast_div_for(1);
+    a.div_tail = fast_div_for(1);
+    a.tiles_per_row = 1;
+    a.div_tiles = fast_div_for(1);
+    if (p.family == kFamElem) {
+        a.nslots = 0;
+        a.ntail = (uint32_t)elems;
+        a.tail_per_row = (uint32_t)elems;
+        a.tail_bytes = 0;
+        a.tail_col_bytes = 0;
+    } else {
+        const int64_t vec = p.vec_elems;
+        const int64_t full = elems / vec;
+        const int64_t rem = elems - full * vec;
+        a.nslots = (uint32_t)full;
+        a.ntail = rem > 0 ? 1u : 0u;
+        a.tail_per_row = 0;
+        a.tail_bytes = (uint32_t)(rem * p.esize);
+        a.tail_col_bytes = (uint32_t)(full * 16);
+    }
+    a.slots_per_row = a.nslots;
+    finish_tiles(p, a);
     Plan q = p;
-    q.rows_mode = 0;
+    q.rows_mode = kWalkContig;
     return launch_one(q, a, cu, s);
 }
 
 // One launch over `nrows` rows of the valid rectangle starting at row `row0`.
 int launch_rows(const Plan& p, KArgs a, const char* const* ordered, char* dst, int64_t row0,
                 int64_t nrows, int cu, hipStream_t s) {
-    const int64_t vec = p.vec_elems;
     const int64_t byte_off = row0 * p.ld * p.esize;
     for (int r = 0; r < p.nranks; ++r) a.src[r] = ordered[r] + byte_off;
     a.dst = dst + byte_off;
-    const int64_t per_row = (p.valid_cols + vec - 1) / vec;
-    a.nvec_row = (uint32_t)per_row;
-    a.tail = (uint32_t)(p.valid_cols - (per_row - 1) * vec);
-    a.nslots = (uint32_t)(per_row * nrows);
+    a.extent = (uint32_t)(((nrows - 1) * p.ld + p.valid_cols) * p.esize);
     a.ld_bytes = nrows > 1 ? (uint32_t)(p.ld * p.esize) : 0u;
-    a.div_row = fast_div_for(a.nvec_row);
-    const int64_t per_tile = (int64_t)256 * p.unroll;
-    a.ntiles = (uint32_t)((a.nslots + per_tile - 1) / per_tile);
+    a.tiles_per_row = 1;
+    a.div_tiles = fast_div_for(1);
+    if (p.family == kFamElem) {
+        a.nslots = 0;
+        a.slots_per_row = 0;
+        a.div_slots = fast_div_for(1);
+        a.ntail = (uint32_t)(nrows * p.valid_cols);
+        a.tail_per_row = (uint32_t)p.valid_cols;
+        a.div_tail = fast_div_for((uint32_t)p.valid_cols);
+        a.tail_bytes = 0;
+        a.tail_col_bytes = 0;
+    } else {
+        const int64_t vec = p.vec_elems;
+        const int64_t full = p.valid_cols / vec;         // full slots per row
+        const int64_t rem = p.valid_cols - full * vec;   // remainder elements per row
+        a.slots_per_row = (uint32_t)full;
+        a.nslots = (uint32_t)(full * nrows);
+        a.div_slots = fast_div_for(full > 0 ? (uint32_t)full : 1u);
+        a.ntail = rem > 0 ? (uint32_t)nrows : 0u;
+        a.tail_per_row = 0;
+        a.div_tail = fast_div_for(1);
+        a.tail_bytes = (uint32_t)(rem * p.esize);
+        a.tail_col_bytes = (uint32_t)(full * 16);
+    }
+    finish_tiles(p, a);
+    if (p.rows_mode == kWalkRowTiles) {
+        const uint64_t per_tile = (uint64_t)kBlock * p.unroll;
+        a.tiles_per_row = (uint32_t)((a.slots_per_row + per_tile - 1) / per_tile);
+        a.div_tiles = fast_div_for(a.tiles_per_row);
+        const uint32_t tail_tiles = a.total_tiles - a.main_tiles;
+        a.main_tiles = (uint32_t)nrows * a.tiles_per_row;
+        a.total_tiles = a.main_tiles + tail_tiles;
+    }
     return launch_one(p, a, cu, s);
 }
 

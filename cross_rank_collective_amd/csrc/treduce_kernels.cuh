@@ -13,22 +13,46 @@
 //
 // Work decomposition.  The valid rectangle is cut into slots: a slot is a
 // run of VEC consecutive elements of one row (16 bytes on the vector path,
-// one element on the element-wise path).  Row i holds nvec_row slots; the
-// last one is partial when valid_cols is not a multiple of VEC and then
-// carries only `tail` valid elements -- the analog of the pages' partial
-// column chunk with a dynamic valid extent.  Slots are numbered row-major.
-// A tile is BLOCK * U consecutive slots, and block b takes tiles b, b+G,
-// b+2G, ... of a persistent grid of G blocks (the pages' block-cyclic walk).
-// Within a tile, thread t owns slots t, t+BLOCK, ..., so every wave
-// instruction moves 64 adjacent 16-byte vectors (1 KiB) of one buffer.
+// one element on the element-wise path).  A tile is BLOCK * U slots, walked
+// in one of three ways:
+//   contiguous  the valid rows follow each other without a gap: one span,
+//               tiles of consecutive slots;
+//   row tiles   the pages' 2-D sliding chunk walk: tile (r, c) is column
+//               chunk c of row r, the last chunk of a row masked -- used
+//               when rows are wide enough to keep the threads busy;
+//   flattened   narrow rows: slots numbered row-major straight through the
+//               rectangle, the row found by a multiply-high division.
+// Block b takes tiles b, b+G, b+2G, ... of a grid of G blocks (the pages'
+// block-cyclic walk).  By default G equals the tile count -- one tile per
+// block, so the hardware dispatcher balances the work over the XCDs as
+// blocks retire; a smaller persistent grid can be requested.  Within a
+// tile, wave w owns U * 64 consecutive slots and lane l the slots l, l+64,
+// ..., so every wave instruction moves 1 KiB of one buffer.
 //
 // Per slot a thread issues the loads of all N sources before it combines
 // anything -- the many waves in flight on a CU take the place of the pages'
 // ping-pong recv tiles -- then folds them in the fixed order (root first,
 // then ascending rank; the host passes the pointers already in that order),
-// rounding to the element type after every step, and stores the result with
-// a non-temporal store.  Elements outside the valid rectangle are never read
-// or written.
+// rounding to the element type after every step, and stores the result.
+// Elements outside the valid rectangle are never read or written.
+//
+// Memory path.  Every access is a buffer instruction against a resource
+// whose record count is the byte extent this launch may touch, so the
+// hardware drops any access past it (loads return zero, stores are
+// discarded): slots past the end of the work are given an offset beyond
+// the extent instead of a branch.  Source loads are non-temporal (the data
+// is used once); stores are device-scope (sc1), which writes through the
+// XCD's L2 to memory -- on MI355X this measured faster for a read-mostly
+// stream than non-temporal or default stores.
+//
+// Ragged edges.  Full 16-byte slots form the main tiles; the valid bytes
+// after the last full slot of each row (fewer than 16), or at the end of a
+// contiguous span, form separate tail tiles in which one thread moves one
+// row's remainder with at most two exact-size accesses per buffer (12 + 2
+// bytes for seven 16-bit elements), so nothing outside the valid rectangle
+// is touched.  The main tiles are therefore branch-free.  The element-wise
+// path (data not 16-byte aligned) has no main tiles: its tail tiles carry
+// every element of the rectangle, one element per access.
 //
 // Combines on gfx950 (element type kept after every step):
 //   f32  sum v_add_f32, prod v_mul_f32, max/min v_maximum3_f32 / v_minimum3_f32
@@ -54,14 +78,10 @@
 
 namespace ptored {
 
-#define PTORED_GLOBAL __attribute__((address_space(1)))
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-
-constexpr int kBlock = 256;
 
 // ------------------------------------------------------------------------
 // Combine on one 32-bit word: one f32 / i32 element, or two bf16 / f16
@@ -275,43 +295,90 @@ struct Acc<PTORED_BF16, PTORED_MIN> {
 };
 
 // ------------------------------------------------------------------------
-// Memory access helpers (global address space, 32-bit byte offsets so the
-// loads use one offset VGPR against each source's SGPR base).
+// Memory access: buffer instructions with a per-launch record count.
 // ------------------------------------------------------------------------
 
-template <bool NT>
-__device__ __forceinline__ u32x4 load16(const void* base, uint32_t off) {
-    const PTORED_GLOBAL u32x4* p =
-        (const PTORED_GLOBAL u32x4*)((const PTORED_GLOBAL char*)base + off);
-    if constexpr (NT) {
-        return __builtin_nontemporal_load(p);
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle, stride 0.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy bits of the buffer instructions (gfx950): nt for loads,
+// sc1 (device scope, write-through of the XCD's L2) for stores.
+constexpr int kLoadPolicy = 2;
+constexpr int kStorePolicy = 16;
+// An offset no launch extent reaches (extents are capped at 2^31 bytes).
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t extent) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)extent,
+                                             kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
+}
+__device__ __forceinline__ void store16(rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStorePolicy);
+}
+// One element of ES bytes, zero-extended into a word (lane 0).
+template <int ES>
+__device__ __forceinline__ uint32_t load_elem(rsrc_t r, uint32_t off) {
+    if constexpr (ES == 4) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadPolicy);
     } else {
-        return *p;
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kLoadPolicy);
     }
 }
-__device__ __forceinline__ void store16(void* base, uint32_t off, u32x4 v) {
-    PTORED_GLOBAL u32x4* p = (PTORED_GLOBAL u32x4*)((PTORED_GLOBAL char*)base + off);
-    __builtin_nontemporal_store(v, p);
-}
-// One element of ES bytes, zero-extended into a word.
 template <int ES>
-__device__ __forceinline__ uint32_t load_elem(const void* base, uint32_t off) {
+__device__ __forceinline__ void store_elem(rsrc_t r, uint32_t off, uint32_t v) {
     if constexpr (ES == 4) {
-        return *(const PTORED_GLOBAL uint32_t*)((const PTORED_GLOBAL char*)base + off);
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kStorePolicy);
     } else {
-        return *(const PTORED_GLOBAL uint16_t*)((const PTORED_GLOBAL char*)base + off);
-    }
-}
-template <int ES>
-__device__ __forceinline__ void store_elem(void* base, uint32_t off, uint32_t v) {
-    if constexpr (ES == 4) {
-        *(PTORED_GLOBAL uint32_t*)((PTORED_GLOBAL char*)base + off) = v;
-    } else {
-        *(PTORED_GLOBAL uint16_t*)((PTORED_GLOBAL char*)base + off) = (uint16_t)v;
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, kStorePolicy);
     }
 }
 
-// Quotient by the slots-per-row count without a divide: the multiply-high
+// Bytes [0, TB) of a 16-byte slot, TB < 16 and a multiple of 2, as at most
+// two accesses (12, 8 or 4 bytes, then 2), into the low words of a vector;
+// the words past TB are zero.
+template <int TB>
+__device__ __forceinline__ u32x4 load_partial(rsrc_t r, uint32_t off) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    constexpr int big = TB >= 12 ? 12 : (TB >= 8 ? 8 : (TB >= 4 ? 4 : 0));
+    if constexpr (big == 12) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, kLoadPolicy);
+        v[0] = w[0]; v[1] = w[1]; v[2] = w[2];
+    } else if constexpr (big == 8) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadPolicy);
+        v[0] = w[0]; v[1] = w[1];
+    } else if constexpr (big == 4) {
+        v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadPolicy);
+    }
+    if constexpr (TB - big == 2) {
+        v[big / 4] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off + big, 0, kLoadPolicy);
+    }
+    return v;
+}
+template <int TB>
+__device__ __forceinline__ void store_partial(rsrc_t r, uint32_t off, u32x4 v) {
+    constexpr int big = TB >= 12 ? 12 : (TB >= 8 ? 8 : (TB >= 4 ? 4 : 0));
+    if constexpr (big == 12) {
+        typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+        const u32x3 w = {v[0], v[1], v[2]};
+        __builtin_amdgcn_raw_buffer_store_b96(w, r, off, 0, kStorePolicy);
+    } else if constexpr (big == 8) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = {v[0], v[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kStorePolicy);
+    } else if constexpr (big == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(v[0], r, off, 0, kStorePolicy);
+    }
+    if constexpr (TB - big == 2) {
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v[big / 4], r, off + big, 0,
+                                             kStorePolicy);
+    }
+}
+
+// Quotient by a per-launch constant without a divide: the multiply-high
 // method of Granlund and Montgomery ("Division by invariant integers using
 // multiplication", PLDI 1994, Fig. 4.1), exact for every 32-bit dividend.
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& d) {
@@ -321,159 +388,226 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& d) {
 
 // Block index remapped so that the blocks the hardware places on one XCD
 // (it deals consecutive workgroups round-robin over the 8 XCDs) get one
-// contiguous range of logical indices: each XCD then sweeps its own band of
-// every grid-stride pass instead of every eighth tile.
+// contiguous range of logical indices (persistent grids only).
 __device__ __forceinline__ uint32_t logical_block(uint32_t b, uint32_t grid, bool remap) {
     if (!remap || (grid & 7u) != 0u) return b;
     return (b & 7u) * (grid >> 3) + (b >> 3);
 }
 
-// Byte offset and valid element count of slot s.
-template <bool ROWS, int VEC, int ES>
-__device__ __forceinline__ void slot_geometry(const KArgs& a, uint32_t s, uint32_t& off,
-                                              uint32_t& cnt) {
-    if (s >= a.nslots) {
-        off = 0;
-        cnt = 0;
-        return;
-    }
-    if constexpr (ROWS) {
-        const uint32_t row = fast_div(s, a.div_row);
-        const uint32_t v = s - row * a.nvec_row;
-        off = row * a.ld_bytes + v * (uint32_t)(VEC * ES);
-        cnt = (v + 1u == a.nvec_row) ? a.tail : (uint32_t)VEC;
+// Byte offset of full slot s (16 bytes) in the flattened walks, or
+// kOutOfRange past the end.
+template <int WALK>
+__device__ __forceinline__ uint32_t slot_offset(const KArgs& a, uint32_t s) {
+    if (s >= a.nslots) return kOutOfRange;
+    if constexpr (WALK == kWalkFlat) {
+        const uint32_t row = fast_div(s, a.div_slots);
+        return row * a.ld_bytes + (s - row * a.slots_per_row) * 16u;
     } else {
-        off = s * (uint32_t)(VEC * ES);
-        cnt = (s + 1u == a.nslots) ? a.tail : (uint32_t)VEC;
+        return s * 16u;
     }
 }
 
-// Fold all ranks of one element (partial-slot path and element-wise
-// kernels): the same order and combine as the vector path, one lane.
-template <int DT, int OP, int ES>
-__device__ __forceinline__ void reduce_one_element(const KArgs& a, uint32_t off) {
+// Byte offset of element q of the element-wise path, or kOutOfRange past the end.
+template <int WALK, int ES>
+__device__ __forceinline__ uint32_t tail_offset(const KArgs& a, uint32_t q) {
+    if (q >= a.ntail) return kOutOfRange;
+    if constexpr (WALK != kWalkContig) {
+        const uint32_t row = fast_div(q, a.div_tail);
+        return row * a.ld_bytes + a.tail_col_bytes + (q - row * a.tail_per_row) * (uint32_t)ES;
+    } else {
+        return a.tail_col_bytes + q * (uint32_t)ES;
+    }
+}
+
+// Fold of one word from NR (compile-time) loaded values, in order.
+template <int DT, int OP, int NR, int U>
+__device__ __forceinline__ uint32_t fold_word(const u32x4 (&x)[NR][U], int u, int w) {
     Acc<DT, OP> acc;
-    acc.init(load_elem<ES>(a.src[0], off));
-    for (uint32_t k = 1; k < a.nranks; ++k) acc.add(load_elem<ES>(a.src[k], off));
-    store_elem<ES>(a.dst, off, acc.get());
+    acc.init(x[0][u][w]);
+#pragma unroll
+    for (int k = 1; k + 1 < NR; k += 2) acc.add2(x[k][u][w], x[k + 1][u][w]);
+    if constexpr (NR > 1 && (NR - 1) % 2 == 1) acc.add(x[NR - 1][u][w]);
+    return acc.get();
 }
 
-// Fold of NR sources (compile-time count) for U full 16-byte slots.
-template <int DT, int OP, int NR, int U, bool NT>
-__device__ __forceinline__ void reduce_vec_fixed(const KArgs& a, const uint32_t (&off)[U]) {
-    u32x4 x[NR][U];
+// One main tile: U full 16-byte slots per thread, NR sources.  Row tiles:
+// tile t is column chunk c of row r (t = r * tiles_per_row + c, split on
+// the scalar unit), so every wave's 1 KiB run starts 1 KiB into a row and
+// never shares a cache line with another wave; flattened walks number the
+// slots straight through.
+template <int DT, int OP, int NR, int U, int WALK>
+__device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t in_tile = wave * (uint32_t)(64 * U) + lane;
+    uint32_t off[U];
+    if constexpr (WALK == kWalkRowTiles) {
+        const uint32_t row = fast_div(t, a.div_tiles);
+        const uint32_t v0 = (t - row * a.tiles_per_row) * (uint32_t)(kBlock * U) + in_tile;
+        const uint32_t row_off = row * a.ld_bytes;
 #pragma unroll
-    for (int k = 0; k < NR; ++k)
-#pragma unroll
-        for (int u = 0; u < U; ++u) x[k][u] = load16<NT>(a.src[k], off[u]);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        u32x4 out;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            Acc<DT, OP> acc;
-            acc.init(x[0][u][w]);
-            int k = 1;
-#pragma unroll
-            for (; k + 1 < NR; k += 2) acc.add2(x[k][u][w], x[k + 1][u][w]);
-            if constexpr ((NR - 1) % 2 == 1) acc.add(x[NR - 1][u][w]);
-            out[w] = acc.get();
+        for (int u = 0; u < U; ++u) {
+            const uint32_t v = v0 + (uint32_t)(u * 64);
+            off[u] = v < a.slots_per_row ? row_off + v * 16u : kOutOfRange;
         }
-        store16(a.dst, off[u], out);
+    } else {
+        const uint32_t base = t * (uint32_t)(kBlock * U) + in_tile;
+#pragma unroll
+        for (int u = 0; u < U; ++u) off[u] = slot_offset<WALK>(a, base + (uint32_t)(u * 64));
+    }
+    const rsrc_t rd = make_rsrc(a.dst, a.extent);
+    if constexpr (NR > 0) {
+        u32x4 x[NR][U];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const rsrc_t r = make_rsrc(a.src[k], a.extent);
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[k][u] = load16(r, off[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            u32x4 out;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[w] = fold_word<DT, OP, NR, U>(x, u, w);
+            store16(rd, off[u], out);
+        }
+    } else {
+        // Runtime rank count: groups of four sources in flight, then the
+        // remainder one at a time, always in rank order.
+        Acc<DT, OP> acc[U][4];
+        {
+            const rsrc_t r = make_rsrc(a.src[0], a.extent);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const u32x4 x0 = load16(r, off[u]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) acc[u][w].init(x0[w]);
+            }
+        }
+        uint32_t k = 1;
+        for (; k + 4 <= a.nranks; k += 4) {
+            u32x4 x[4][U];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const rsrc_t r = make_rsrc(a.src[k + g], a.extent);
+#pragma unroll
+                for (int u = 0; u < U; ++u) x[g][u] = load16(r, off[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    acc[u][w].add2(x[0][u][w], x[1][u][w]);
+                    acc[u][w].add2(x[2][u][w], x[3][u][w]);
+                }
+        }
+        for (; k < a.nranks; ++k) {
+            const rsrc_t r = make_rsrc(a.src[k], a.extent);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const u32x4 x = load16(r, off[u]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) acc[u][w].add(x[w]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            u32x4 out;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[w] = acc[u][w].get();
+            store16(rd, off[u], out);
+        }
     }
 }
 
-// Fold of a runtime number of sources for one full 16-byte slot: groups of
-// four loads in flight, then the remainder one by one, in rank order.
-template <int DT, int OP, bool NT>
-__device__ __forceinline__ void reduce_vec_runtime(const KArgs& a, uint32_t off) {
+// One tail tile of the element-wise path: kElemUnroll elements per thread,
+// element by element.
+template <int DT, int OP, int ES, int NR, int WALK>
+__device__ __forceinline__ void element_tile(const KArgs& a, uint32_t t) {
+    constexpr int TU = kElemUnroll;
+    const uint32_t base = t * (uint32_t)(kBlock * TU) + threadIdx.x;
+    uint32_t off[TU];
+#pragma unroll
+    for (int u = 0; u < TU; ++u) off[u] = tail_offset<WALK, ES>(a, base + (uint32_t)(u * kBlock));
+    const rsrc_t rd = make_rsrc(a.dst, a.extent);
+    Acc<DT, OP> acc[TU];
+    {
+        const rsrc_t r = make_rsrc(a.src[0], a.extent);
+#pragma unroll
+        for (int u = 0; u < TU; ++u) acc[u].init(load_elem<ES>(r, off[u]));
+    }
+    const uint32_t n = NR > 0 ? (uint32_t)NR : a.nranks;
+    for (uint32_t k = 1; k < n; ++k) {
+        const rsrc_t r = make_rsrc(a.src[k], a.extent);
+        uint32_t x[TU];
+#pragma unroll
+        for (int u = 0; u < TU; ++u) x[u] = load_elem<ES>(r, off[u]);
+#pragma unroll
+        for (int u = 0; u < TU; ++u) acc[u].add(x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < TU; ++u) store_elem<ES>(rd, off[u], acc[u].get());
+}
+
+// One row remainder of TB bytes (the pages' partial column chunk with a
+// dynamic valid extent): loaded from every source, folded lane-wise in the
+// same order as the main tiles, stored with the same two exact accesses.
+template <int DT, int OP, int NR, int TB>
+__device__ __forceinline__ void row_tail(const KArgs& a, uint32_t off) {
+    const rsrc_t rd = make_rsrc(a.dst, a.extent);
     Acc<DT, OP> acc[4];
     {
-        const u32x4 x0 = load16<NT>(a.src[0], off);
+        const u32x4 x0 = load_partial<TB>(make_rsrc(a.src[0], a.extent), off);
 #pragma unroll
         for (int w = 0; w < 4; ++w) acc[w].init(x0[w]);
     }
-    uint32_t k = 1;
-    for (; k + 4 <= a.nranks; k += 4) {
-        u32x4 x[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) x[g] = load16<NT>(a.src[k + g], off);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            acc[w].add2(x[0][w], x[1][w]);
-            acc[w].add2(x[2][w], x[3][w]);
-        }
-    }
-    for (; k < a.nranks; ++k) {
-        const u32x4 x = load16<NT>(a.src[k], off);
+    const uint32_t n = NR > 0 ? (uint32_t)NR : a.nranks;
+    for (uint32_t k = 1; k < n; ++k) {
+        const u32x4 x = load_partial<TB>(make_rsrc(a.src[k], a.extent), off);
 #pragma unroll
         for (int w = 0; w < 4; ++w) acc[w].add(x[w]);
     }
     u32x4 out;
 #pragma unroll
     for (int w = 0; w < 4; ++w) out[w] = acc[w].get();
-    store16(a.dst, off, out);
+    store_partial<TB>(rd, off, out);
 }
 
-// Vector kernel: 16-byte slots, NR sources (NR == 0: runtime count).
-// ES = element size in bytes, U = slots per thread per tile.
-template <int DT, int OP, int ES, int NR, int U, bool ROWS, bool NT>
-__global__ __launch_bounds__(kBlock) void treduce_vec_kernel(const KArgs a) {
-    constexpr int VEC = 16 / ES;
-    const uint32_t grid = gridDim.x;
-    const uint32_t lb = logical_block(blockIdx.x, grid, a.xcd_remap != 0u);
-    for (uint32_t tile = lb; tile < a.ntiles; tile += grid) {
-        const uint32_t s0 = tile * (uint32_t)(kBlock * U) + threadIdx.x;
-        uint32_t off[U], cnt[U];
-        bool full = true;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            slot_geometry<ROWS, VEC, ES>(a, s0 + (uint32_t)(u * kBlock), off[u], cnt[u]);
-            full = full && (cnt[u] == (uint32_t)VEC);
-        }
-        if (full) {
-            if constexpr (NR > 0) {
-                reduce_vec_fixed<DT, OP, NR, U, NT>(a, off);
-            } else {
-#pragma unroll
-                for (int u = 0; u < U; ++u) reduce_vec_runtime<DT, OP, NT>(a, off[u]);
-            }
-        } else {
-            // Ragged edge: the end of the stream or the partial last slot
-            // of a row.  Full slots still go 16 bytes at a time; a partial
-            // slot goes element by element over its valid elements only.
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (cnt[u] == (uint32_t)VEC) {
-                    if constexpr (NR > 0) {
-                        const uint32_t one[1] = {off[u]};
-                        reduce_vec_fixed<DT, OP, NR, 1, NT>(a, one);
-                    } else {
-                        reduce_vec_runtime<DT, OP, NT>(a, off[u]);
-                    }
-                } else {
-                    for (uint32_t e = 0; e < cnt[u]; ++e)
-                        reduce_one_element<DT, OP, ES>(a, off[u] + e * (uint32_t)ES);
-                }
-            }
-        }
+// One tail tile of the vector path: kBlock row remainders, one per thread.
+template <int DT, int OP, int ES, int NR>
+__device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
+    const uint32_t q = t * (uint32_t)kBlock + threadIdx.x;
+    if (q >= a.ntail) return;
+    const uint32_t off = q * a.ld_bytes + a.tail_col_bytes;
+    switch (a.tail_bytes) {  // uniform over the launch
+    case 2: if constexpr (ES == 2) row_tail<DT, OP, NR, 2>(a, off); break;
+    case 4: row_tail<DT, OP, NR, 4>(a, off); break;
+    case 6: if constexpr (ES == 2) row_tail<DT, OP, NR, 6>(a, off); break;
+    case 8: row_tail<DT, OP, NR, 8>(a, off); break;
+    case 10: if constexpr (ES == 2) row_tail<DT, OP, NR, 10>(a, off); break;
+    case 12: row_tail<DT, OP, NR, 12>(a, off); break;
+    case 14: if constexpr (ES == 2) row_tail<DT, OP, NR, 14>(a, off); break;
+    default: break;
     }
 }
 
-// Element-wise kernel for data that is not 16-byte aligned: one element per
-// slot, runtime rank count.  U slots per thread per tile.
-template <int DT, int OP, int ES, bool ROWS>
-__global__ __launch_bounds__(kBlock) void treduce_elem_kernel(const KArgs a) {
-    constexpr int U = kElemUnroll;
+// The reduction kernel.  Tiles [0, main_tiles) are main tiles, the rest
+// tail tiles; block b takes tiles b, b + G, ... (one tile per block when
+// G equals the tile count).  NR == 0: runtime rank count.  VEC: 16-byte
+// main tiles with row-remainder tails; otherwise element tiles only.
+// WALK: kWalkContig, kWalkRowTiles or kWalkFlat.
+template <int DT, int OP, int ES, int NR, int U, int WALK, bool VEC>
+__global__ __launch_bounds__(kBlock) void treduce_kernel(const KArgs a) {
     const uint32_t grid = gridDim.x;
-    const uint32_t lb = logical_block(blockIdx.x, grid, a.xcd_remap != 0u);
-    for (uint32_t tile = lb; tile < a.ntiles; tile += grid) {
-        const uint32_t s0 = tile * (uint32_t)(kBlock * U) + threadIdx.x;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            uint32_t off, cnt;
-            slot_geometry<ROWS, 1, ES>(a, s0 + (uint32_t)(u * kBlock), off, cnt);
-            if (cnt) reduce_one_element<DT, OP, ES>(a, off);
+    for (uint32_t t = logical_block(blockIdx.x, grid, a.xcd_remap != 0u); t < a.total_tiles;
+         t += grid) {
+        if constexpr (VEC) {
+            if (t < a.main_tiles) {
+                main_tile<DT, OP, NR, U, WALK>(a, t);
+            } else {
+                row_tail_tile<DT, OP, ES, NR>(a, t - a.main_tiles);
+            }
+        } else {
+            element_tile<DT, OP, ES, NR, WALK>(a, t);
         }
     }
 }

@@ -20,20 +20,35 @@ struct FastDiv {
     uint32_t sh2;
 };
 
-// Kernel arguments of one launch (passed by value; ~600 bytes of kernarg).
+// Kernel arguments of one launch (passed by value; ~620 bytes of kernarg).
 struct KArgs {
     // src[0] is the root's buffer, then the other ranks in ascending order:
     // the kernels fold src[0], src[1], ... in index order.
     const void* src[PTORED_MAX_RANKS];
     void* dst;
     uint32_t nranks;
-    uint32_t ntiles;    // tiles of kBlock * U slots
-    uint32_t nslots;    // slots in this launch
-    uint32_t nvec_row;  // slots per row (row walk)
-    uint32_t ld_bytes;  // row pitch in bytes (row walk)
-    uint32_t tail;      // valid elements of the last slot of a row / of the stream
-    FastDiv div_row;    // division by nvec_row
-    uint32_t xcd_remap; // 1: per-XCD contiguous tile bands
+    uint32_t extent;         // bytes of every buffer this launch may touch (from its base)
+    uint32_t main_tiles;     // tiles of full 16-byte slots
+    uint32_t total_tiles;    // main tiles, then tail tiles of ragged elements
+    uint32_t nslots;         // full 16-byte slots
+    uint32_t slots_per_row;  // full slots per row (row walk)
+    uint32_t ld_bytes;       // row pitch in bytes (row walk)
+    uint32_t ntail;          // tail items: row remainders (vector path) or elements
+    uint32_t tail_per_row;   // elements per row (element-wise row walk)
+    uint32_t tail_bytes;     // bytes of every row remainder (vector path), < 16
+    uint32_t tail_col_bytes; // byte offset in a row (or the span) of the remainder
+    uint32_t tiles_per_row;  // column chunks per row (row tiles)
+    FastDiv div_tiles;       // division by tiles_per_row
+    FastDiv div_slots;       // division by slots_per_row
+    FastDiv div_tail;        // division by tail_per_row
+    uint32_t xcd_remap;      // 1: per-XCD contiguous tile bands (persistent grids)
+};
+
+// Walks of the valid rectangle (values of Plan::walk and ptored_plan_info.rows_mode).
+enum Walk : int {
+    kWalkContig = 0,    // one contiguous span
+    kWalkRowTiles = 1,  // tile = (row, column chunk)
+    kWalkFlat = 2,      // slots numbered straight through the rows
 };
 
 // Kernel families.
@@ -52,12 +67,11 @@ struct Plan {
     int op;
     int nranks;
     int esize;
-    int rows_mode;      // 1: 2-D row walk, 0: one contiguous span
+    int rows_mode;      // Walk
     int vec_elems;      // elements per slot
-    int unroll;         // slots per thread per tile
-    bool nt_loads;
+    int unroll;         // slots per thread per main tile
     bool xcd_remap;
-    int blocks_per_cu;
+    int blocks_per_cu;  // 0: one tile per block; > 0: persistent grid; < 0: at occupancy
     // geometry of the whole call
     int64_t valid_rows;
     int64_t valid_cols;
@@ -68,14 +82,18 @@ struct Plan {
     int64_t launches;
 };
 
-// Unroll (slots per thread per tile) of the fixed-N vector kernel: enough
-// 16-byte loads in flight per thread (N * U of them) to cover HBM latency,
-// without exhausting VGPRs at large N.
+// Threads per workgroup (four waves).
+constexpr int kBlock = 256;
+
+// Unroll (16-byte slots per thread per main tile).  Bandwidth sweeps on
+// MI355X over tiles of 1 to 16 slots per thread: the smallest tiles were
+// fastest for N >= 3 -- one slot per thread, all N loads of it in flight,
+// many small blocks for the dispatcher to balance -- and two slots for N <= 2.
 constexpr int unroll_for(int nranks) {
-    return nranks <= 2 ? 4 : (nranks <= 4 ? 4 : (nranks <= 8 ? 2 : 1));
+    return nranks <= 2 ? 2 : 1;
 }
-constexpr int kElemUnroll = 4;
-constexpr int kRuntimeUnroll = 2;
+constexpr int kElemUnroll = 4;     // elements per thread, element-wise path
+constexpr int kRuntimeUnroll = 2;  // slots per thread, runtime rank count
 
 // Launch one kernel of the plan's family on `a`, on a persistent grid sized
 // for `cu_count` compute units.

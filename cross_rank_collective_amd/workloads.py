@@ -91,6 +91,24 @@ WORKLOADS = {
 # The largest N-way reduce: 16 ranks.
 HEADLINE = "n16_i32_4096x4096"
 
+# A plain 1 GiB copy (one rank): reads and writes a known number of bytes,
+# used to scale hardware traffic counters to bytes.
+CALIBRATION = {
+    w.name: w
+    for w in [
+        Workload("n1_i32_16384x16384_copy", 1, "i32", ("sum",), 16384, 16384, 16384, 16384,
+                 16384, 0, "int_pm2^20", 6000),
+    ]
+}
+
+
+def find(name: str) -> Workload:
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name in CALIBRATION:
+        return CALIBRATION[name]
+    raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS) + sorted(CALIBRATION)}")
+
 
 def _f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     import torch  # CPU conversion only; rounds to nearest, ties to even

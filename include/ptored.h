@@ -101,9 +101,10 @@ typedef enum ptored_status {
  * Errors are checked before any HIP call, in this order: INVALID_ARG (N or
  * root out of range, a null pointer, a negative size, cols > ld,
  * valid_rows > rows, valid_cols > cols, a size whose byte extent overflows),
- * UNSUPPORTED (dtype or op outside the enums), OVERLAP.  ERR_HIP is returned
- * when the launch fails.  Misaligned pointers or strides are not errors:
- * they select an element-wise kernel.
+ * UNSUPPORTED (dtype or op outside the enums), INVALID_ARG (a pointer not
+ * aligned to the element size), OVERLAP.  ERR_HIP is returned when the
+ * launch fails.  Pointers or row pitches that are not 16-byte aligned are
+ * not errors: they select an element-wise kernel.
  */
 int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int64_t rows,
                    int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
@@ -113,15 +114,19 @@ int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int
 #define PTORED_FORCE_ELEMENTWISE 0x1u /* element-wise kernel even when 16-B aligned */
 #define PTORED_FORCE_ROWS 0x2u        /* 2-D row walk even for a contiguous region */
 #define PTORED_FORCE_RUNTIME_N 0x4u   /* rank-count loop instead of an unrolled N */
-#define PTORED_NO_XCD_REMAP 0x8u      /* plain block order instead of per-XCD ranges */
-#define PTORED_NT_LOADS 0x10u         /* non-temporal source loads */
+#define PTORED_NO_XCD_REMAP 0x8u      /* persistent grid: plain block order, not per-XCD bands */
+#define PTORED_ROW_TILES 0x10u        /* 2-D region: tiles of one row's column chunk (the pages'
+                                         2-D sliding chunk walk) instead of slots numbered
+                                         straight through the rows */
 
 /* Launch choices of ptored_treduce_ex. */
 typedef struct ptored_tuning {
-    uint32_t flags;         /* PTORED_FORCE_* / PTORED_NO_XCD_REMAP / PTORED_NT_LOADS */
-    int32_t blocks_per_cu;  /* workgroups per compute unit in the persistent grid; 0 = auto */
-    int64_t max_launch_bytes; /* split a call into launches of at most this many bytes of
-                                 row span per buffer; 0 = auto (2^31) */
+    uint32_t flags;          /* PTORED_FORCE_* and PTORED_NO_XCD_REMAP bits */
+    int32_t blocks_per_cu;   /* 0 = one workgroup per tile (default); > 0 = persistent grid
+                                of that many workgroups per compute unit; < 0 = persistent
+                                grid at the kernel's occupancy */
+    int64_t max_launch_bytes; /* split a call into launches that touch at most this many
+                                 bytes of each buffer; 0 = auto (2^31) */
 } ptored_tuning;
 
 /* ptored_treduce with explicit launch choices; `tuning` may be NULL (= all

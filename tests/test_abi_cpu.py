@@ -75,6 +75,7 @@ def _call(n=2, root=0, dst=D, rows=4, cols=4, ld=4, vr=4, vc=4, dtype=0, op=0, s
     (dict(vr=5), -1), (dict(vc=5, cols=4, ld=8), -1), (dict(rows=1 << 40, ld=1 << 30), -1),
     (dict(dtype=4), -2), (dict(dtype=-1), -2), (dict(op=4), -2), (dict(op=-1), -2),
     (dict(dst=A[1] + 4), -3), (dict(dst=A[0] - 8), -3),
+    (dict(dst=D + 2), -1), (dict(srcs=[A[0], A[1] + 1]), -1), (dict(dst=D + 1, dtype=2), -1),
 ])
 def test_argument_errors_before_any_hip_call(kw, status):
     assert _call(**kw) == status
@@ -83,6 +84,7 @@ def test_argument_errors_before_any_hip_call(kw, status):
 def test_invalid_beats_unsupported_beats_overlap():
     assert _call(root=9, dtype=9) == -1
     assert _call(dtype=9, dst=A[1] + 4) == -2
+    assert _call(dst=A[1] + 2) == -1  # misaligned element pointer before overlap
 
 
 def test_empty_region_returns_ok_without_launch():
@@ -126,10 +128,24 @@ def test_plan_paths():
 def test_plan_walk_and_slots():
     info = _plan(rows=8, cols=8, ld=8, vr=8, vc=8)  # contiguous f32
     assert (info.rows_mode, info.vec_elems, info.slots, info.launches) == (0, 4, 16, 1)
-    info = _plan(rows=8, cols=10, ld=12, vr=7, vc=10)  # 2-D: 3 slots per row
-    assert (info.rows_mode, info.slots) == (1, 21)
+    info = _plan(rows=8, cols=10, ld=12, vr=7, vc=10)  # narrow rows: flattened, 3 slots/row
+    assert (info.rows_mode, info.slots) == (2, 21)
     info = _plan(rows=8, cols=8, ld=8, vr=8, vc=8, tuning=B.tuning(flags=B.PTORED_FORCE_ROWS))
-    assert (info.rows_mode, info.slots) == (1, 16)
+    assert (info.rows_mode, info.slots) == (2, 16)
+    # wide rows: flattened by default; row tiles (tile = row x column chunk) on
+    # request: 1000 f32 = 250 slots in one chunk
+    info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000)
+    assert (info.rows_mode, info.slots) == (2, 60 * 250)
+    rt = B.tuning(flags=B.PTORED_ROW_TILES)
+    info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000, tuning=rt)
+    assert (info.rows_mode, info.slots) == (1, 60 * 250)
+    # 3 chunks of 256 slots for 513 slots: 513/768 of the threads busy -> flattened
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=2052, ld=2056, vr=4, vc=2052, tuning=rt)
+    assert info.rows_mode == 2
+    # 8 or more chunks per row: row tiles whatever the last chunk holds
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=4 * 7 * 256 + 4, ld=7200, vr=4, vc=7172,
+                 tuning=rt)
+    assert info.rows_mode == 1
     info = _plan(rows=1, cols=13, ld=16, vr=1, vc=13, dtype=2)  # one row: contiguous f16
     assert (info.rows_mode, info.vec_elems, info.slots) == (0, 8, 2)
 
@@ -141,7 +157,7 @@ def test_plan_launch_split():
     # rows: 10 rows, pitch 64 B, 40 valid bytes per row, 256-byte launches:
     # (256 - 40) // 64 + 1 = 4 rows per launch -> 3 launches
     info = _plan(rows=10, cols=10, ld=16, vr=10, vc=10, tuning=B.tuning(max_launch_bytes=256))
-    assert (info.rows_mode, info.launches) == (1, 3)
+    assert (info.rows_mode, info.launches) == (2, 3)
     # rows longer than one launch: every row is split into spans
     info = _plan(rows=3, cols=100, ld=104, vr=3, vc=100, tuning=B.tuning(max_launch_bytes=128))
     assert info.launches == 3 * 4
@@ -151,14 +167,14 @@ def test_workload_plans():
     """Each named workload takes the kernel family its shape calls for."""
     want = {
         "n2_f32_16x16": ("vec_fixed", 0),
-        "n4_f32_1024x1024_valid1000x1000": ("vec_fixed", 1),
+        "n4_f32_1024x1024_valid1000x1000": ("vec_fixed", 2),
         "n8_bf16_8192x8192": ("vec_fixed", 0),
         "n16_i32_4096x4096": ("vec_fixed", 0),
-        "n8_f16_8192x12288_valid8191x12287": ("vec_fixed", 1),
+        "n8_f16_8192x12288_valid8191x12287": ("vec_fixed", 2),
     }
     for name, w in W.WORKLOADS.items():
         info = _plan(n=w.nranks, srcs=A[:w.nranks], rows=w.rows, cols=w.cols, ld=w.ld,
                      vr=w.valid_rows, vc=w.valid_cols, dtype=B.DTYPES[w.dtype],
                      op=B.OPS[w.ops[0]])
-        assert (B.PATHS[info.path], info.rows_mode) == want[name], name
+        assert (B.PATHS[info.path], info.rows_mode) == want[name], name  # 2 = flattened
         assert info.launches == 1

@@ -82,10 +82,11 @@ VARIANTS = [
     ("auto", 0, 0),
     ("elementwise", B.PTORED_FORCE_ELEMENTWISE, 0),
     ("rows", B.PTORED_FORCE_ROWS, 0),
+    ("row_tiles", B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES, 0),
     ("runtime_n", B.PTORED_FORCE_RUNTIME_N, 0),
-    ("nt_noremap", B.PTORED_NT_LOADS | B.PTORED_NO_XCD_REMAP, 0),
+    ("persistent_noremap", B.PTORED_NO_XCD_REMAP, 2),
     ("one_block_per_cu", 0, 1),
-    ("block_per_tile", 0, -1),
+    ("persistent_occupancy", 0, -1),
 ]
 
 
@@ -125,6 +126,7 @@ MEDIUM = [
     (64, 512, 512, 64, 512),
     (1, 200003, 200003, 1, 200003),
     (257, 333, 336, 250, 331),
+    (60, 8200, 8200, 60, 8193),   # row tiles: 8 (f32) / 4 (16-bit) chunks per row + remainder
 ]
 
 
@@ -136,6 +138,8 @@ def test_medium_cases_span_many_tiles(dtype):
     for case, (rows, cols, ld, vr, vc) in enumerate(MEDIUM):
         for n, op, vname, flags, bpc in [(4, OPS[case % 4], "auto", 0, 1),
                                          (9, OPS[(case + 1) % 4], "rows", B.PTORED_FORCE_ROWS, 0),
+                                         (6, OPS[(case + 1) % 4], "row_tiles",
+                                          B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES, 0),
                                          (16, OPS[(case + 2) % 4], "auto", 0, 0),
                                          (20, OPS[(case + 3) % 4], "runtime_n", 0, 0),
                                          (3, OPS[case % 4], "elementwise",
@@ -159,11 +163,12 @@ def test_split_into_many_launches(dtype):
     es = ESIZE[dtype]
     for rows, cols, ld, vr, vc, mlb in [(40, 256, 256, 40, 256, 1024),
                                         (40, 250, 264, 37, 249, 3000),
-                                        (5, 3000, 3008, 5, 2999, 512)]:
+                                        (5, 3000, 3008, 5, 2999, 512),
+                                        (12, 4100, 4104, 12, 4099, 40000)]:
         n = 5
         size = (rows - 1) * ld + cols
         srcs = [_rand_elems(dtype, rng, size, wild=0.02) for _ in range(n)]
-        for flags in (0, B.PTORED_FORCE_ELEMENTWISE):
+        for flags in (0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_ROW_TILES):
             t = B.tuning(flags=flags, max_launch_bytes=mlb)
             st_plan, info = B.ptored_treduce_plan([0x100000] * n, n, 1, 0x900000, rows, cols, ld,
                                                   vr, vc, B.DTYPES[dtype], 0, t)
@@ -278,9 +283,9 @@ def test_workload_full_size(name):
     srcs = _workload_srcs(w)
     rng = np.random.default_rng(7)
     full_compare = w.dtype == "i32" or w.buffer_elems <= 1 << 21
-    variants = [("auto", 0)]
+    variants = [("auto", 0), ("row_tiles", B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES)]
     if w.valid_cols == w.ld:
-        variants.append(("rows", B.PTORED_FORCE_ROWS))  # the 2-D walk on the same data
+        variants.append(("rows", B.PTORED_FORCE_ROWS))  # the flattened 2-D walk, same data
     es = w.esize
     for op in w.ops:
         results = []
@@ -309,6 +314,6 @@ def test_workload_full_size(name):
                                          w.valid_cols, lambda k: sentinel(w.dtype, k))
                     seg = got[lo:lo + w.valid_cols]
                     assert compare(w.dtype, seg, want[:w.valid_cols]).all(), (label, r)
-        if len(results) > 1:
-            assert np.array_equal(results[0].view(np.uint8), results[1].view(np.uint8))
+        for other in results[1:]:
+            assert np.array_equal(results[0].view(np.uint8), other.view(np.uint8))
         torch.cuda.empty_cache()
