@@ -66,6 +66,15 @@ def _load():
     lib.oracle_to_double.argtypes = [ctypes.c_int, vp, vp, i64]
     lib.oracle_to_double.restype = None
     lib.oracle_max_ranks.restype = ctypes.c_int
+    lib.oracle_ring_bounds.argtypes = [i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.oracle_ring_bounds.restype = ctypes.c_int
+    lib.oracle_reduce_scatter_ring.argtypes = [ctypes.POINTER(vp), ctypes.c_int,
+                                               ctypes.POINTER(vp), i64, ctypes.c_int,
+                                               ctypes.c_int]
+    lib.oracle_reduce_scatter_ring.restype = ctypes.c_int
+    lib.oracle_accumulate_add.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, i64, i64, i64,
+                                          i64, i64, ctypes.c_int, vp, vp]
+    lib.oracle_accumulate_add.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -104,6 +113,45 @@ def allreduce_inplace(bufs: Sequence[np.ndarray], *, root: int, dtype: str, op: 
                                       ld, valid_rows, valid_cols, DTYPES[dtype], OPS[op])
     if rc != 0:
         raise ValueError(f"oracle_allreduce_inplace rejected its arguments (status {rc})")
+
+
+def ring_bounds(count: int, nranks: int, dtype: str) -> np.ndarray:
+    """Segment boundaries (nranks + 1 of them) of the ring schedule."""
+    lib = _load()
+    out = np.zeros(nranks + 1, dtype=np.int64)
+    rc = lib.oracle_ring_bounds(count, nranks, DTYPES[dtype], out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_ring_bounds rejected its arguments (status {rc})")
+    return out
+
+
+def reduce_scatter_ring(srcs: Sequence[np.ndarray], dsts: Sequence[np.ndarray], *, count: int,
+                        dtype: str, op: str) -> None:
+    """dsts[s][segment s] = ring-order fold of every source over segment s."""
+    lib = _load()
+    _check_buffers(list(srcs) + list(dsts), dtype, 1, count, count)
+    sp = (ctypes.c_void_p * len(srcs))(*[a.ctypes.data for a in srcs])
+    dp = (ctypes.c_void_p * len(dsts))(*[a.ctypes.data for a in dsts])
+    rc = lib.oracle_reduce_scatter_ring(sp, len(srcs), dp, count, DTYPES[dtype], OPS[op])
+    if rc != 0:
+        raise ValueError(f"oracle_reduce_scatter_ring rejected its arguments (status {rc})")
+
+
+def accumulate_add(srcs: Sequence[np.ndarray], dst: np.ndarray, *, dtype: str, rows: int,
+                   cols: int, ld: int, valid_rows: int, valid_cols: int):
+    """dst += every source, in rank order with element rounding; returns the
+    exact sums and the absolute sums over the valid rectangle (float types)."""
+    lib = _load()
+    _check_buffers(list(srcs) + [dst], dtype, rows, ld, cols)
+    ptrs = (ctypes.c_void_p * max(1, len(srcs)))(*[a.ctypes.data for a in srcs])
+    exact = np.zeros(valid_rows * valid_cols, dtype=np.float64)
+    absum = np.zeros(valid_rows * valid_cols, dtype=np.float64)
+    rc = lib.oracle_accumulate_add(ptrs, len(srcs), dst.ctypes.data, rows, cols, ld, valid_rows,
+                                   valid_cols, DTYPES[dtype], exact.ctypes.data,
+                                   absum.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_accumulate_add rejected its arguments (status {rc})")
+    return exact, absum
 
 
 def combine_bits(dtype: str, op: str, a: np.ndarray, b: np.ndarray) -> np.ndarray:

@@ -271,6 +271,96 @@ int oracle_allreduce_inplace(void* const* bufs, int nranks, int root, void* scra
     return 0;
 }
 
+/* Segment boundaries of the ring schedule ([N6] pld.tensor.allreduce, ring
+ * mode): a stream of `count` elements is cut into `nranks` segments at the
+ * balanced boundaries floor(i * count / nranks); for 2-byte elements every
+ * interior boundary is then rounded up to a multiple of 16 elements (32
+ * bytes) and capped at `count`, so short streams may have empty segments.
+ * bounds[0] = 0, bounds[nranks] = count. */
+int oracle_ring_bounds(int64_t count, int nranks, int dtype, int64_t* bounds) {
+    if (count < 0 || nranks < 1 || nranks > OR_MAX_RANKS || !bounds) return -1;
+    if (dtype < OR_F32 || dtype > OR_I32) return -2;
+    bounds[0] = 0;
+    for (int i = 1; i < nranks; ++i) {
+        int64_t b = (int64_t)((__int128)i * count / nranks);
+        if (esize_of(dtype) == 2) {
+            b = (b + 15) / 16 * 16;
+            if (b > count) b = count;
+        }
+        bounds[i] = b;
+    }
+    bounds[nranks] = count;
+    return 0;
+}
+
+/* The reduce-scatter share of the ring schedule on one device: segment s of
+ * the stream is reduced over all ranks and written to dsts[s] (same element
+ * positions).  The partial result of a ring reduce-scatter for segment s
+ * starts at rank s+1 and travels round the ring, each rank folding in its own
+ * value, until it reaches rank s, which folds its value last: the fold order
+ * is s+1, s+2, ..., s+N-1, s (ranks mod N). */
+int oracle_reduce_scatter_ring(const void* const* srcs, int nranks, void* const* dsts,
+                               int64_t count, int dtype, int op) {
+    if (nranks < 1 || nranks > OR_MAX_RANKS || !srcs || !dsts || count < 0) return -1;
+    if (dtype < OR_F32 || dtype > OR_I32 || op < OR_SUM || op > OR_PROD) return -2;
+    int64_t bounds[OR_MAX_RANKS + 1];
+    int rc = oracle_ring_bounds(count, nranks, dtype, bounds);
+    if (rc) return rc;
+    const int es = esize_of(dtype);
+    for (int s = 0; s < nranks; ++s) {
+        for (int64_t j = bounds[s]; j < bounds[s + 1]; ++j) {
+            uint32_t acc = load_bits(srcs[(s + 1) % nranks], j, es);
+            for (int k = 2; k <= nranks; ++k)
+                acc = combine(dtype, op, acc, load_bits(srcs[(s + k) % nranks], j, es));
+            store_bits(dsts[s], j, es, acc);
+        }
+    }
+    return 0;
+}
+
+/* Push-with-add ([N6] pld.tensor.put / remote_store with atomic = kAdd: the
+ * pushed data is added into the peer's slice).  With N ranks pushing into
+ * one slice, dst[i, j] becomes dst[i, j] + src_0[i, j] + ... + src_{N-1}[i, j]
+ * with the additions in an unspecified order.  This reference applies them in
+ * rank order, each addition rounded to the element type (i32 wraps), and
+ * also returns, for the float types, the exact sum (in `exact`, doubles, one
+ * per element of the valid rectangle, row-major) and the sum of absolute
+ * values (in `absum`), from which a test bounds any other order's result. */
+int oracle_accumulate_add(const void* const* srcs, int nranks, void* dst, int64_t rows,
+                          int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
+                          int dtype, double* exact, double* absum) {
+    int rc = check_args(srcs, nranks, 0, dst, rows, cols, ld, valid_rows, valid_cols, dtype,
+                        OR_SUM);
+    if (rc) return rc;
+    const int es = esize_of(dtype);
+    int64_t k = 0;
+    for (int64_t i = 0; i < valid_rows; ++i) {
+        for (int64_t j = 0; j < valid_cols; ++j, ++k) {
+            const int64_t idx = i * ld + j;
+            uint32_t acc = load_bits(dst, idx, es);
+            double ex = 0.0, ab = 0.0;
+            if (dtype != OR_I32) {
+                ex = to_double(dtype, acc);
+                ab = fabs(ex);
+            }
+            for (int r = 0; r < nranks; ++r) {
+                const uint32_t x = load_bits(srcs[r], idx, es);
+                acc = combine(dtype, OR_SUM, acc, x);
+                if (dtype != OR_I32) {
+                    /* summed in double: its own error, at most (N+1) * 2^-53 of
+                     * the absolute sum, is far below any element rounding */
+                    ex += to_double(dtype, x);
+                    ab += fabs(to_double(dtype, x));
+                }
+            }
+            store_bits(dst, idx, es, acc);
+            if (exact) exact[k] = ex;
+            if (absum) absum[k] = ab;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Exported single steps, so tests can pin the arithmetic on its own.        */
 /* ------------------------------------------------------------------------ */
