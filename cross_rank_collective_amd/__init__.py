@@ -11,7 +11,11 @@ from .binding import (  # noqa: F401
     PtoredError,
     load,
     ptored_abi_version,
+    ptored_accumulate_add,
+    ptored_allreduce,
     ptored_max_ranks,
+    ptored_reduce_scatter_ring,
+    ptored_ring_bounds,
     ptored_status_string,
     ptored_treduce,
     ptored_treduce_ex,

@@ -6,8 +6,10 @@ sizes.  torch provides device memory and the stream.  There is no fallback:
 if the library is missing or a call fails, an exception is raised.
 
 The C functions keep their names: ``ptored_treduce``, ``ptored_treduce_ex``,
-``ptored_treduce_plan``, ``ptored_status_string``, ``ptored_abi_version``,
-``ptored_max_ranks``.  ``treduce`` is the tensor-level convenience wrapper.
+``ptored_treduce_plan``, ``ptored_allreduce``, ``ptored_ring_bounds``,
+``ptored_reduce_scatter_ring``, ``ptored_accumulate_add``,
+``ptored_status_string``, ``ptored_abi_version``, ``ptored_max_ranks``.
+``treduce`` is the tensor-level convenience wrapper.
 """
 
 from __future__ import annotations
@@ -77,6 +79,17 @@ def load() -> ctypes.CDLL:
     lib.ptored_treduce_plan.argtypes = common + [ctypes.POINTER(ptored_tuning),
                                                  ctypes.POINTER(ptored_plan_info)]
     lib.ptored_treduce_plan.restype = i32
+    lib.ptored_allreduce.argtypes = [ctypes.POINTER(vp), i32, i32, i64, i64, i64, i64, i64, i32,
+                                     i32, ctypes.POINTER(ptored_tuning), vp]
+    lib.ptored_allreduce.restype = i32
+    lib.ptored_ring_bounds.argtypes = [i64, i32, i32, ctypes.POINTER(i64)]
+    lib.ptored_ring_bounds.restype = i32
+    lib.ptored_reduce_scatter_ring.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(vp), i64,
+                                               i32, i32, ctypes.POINTER(ptored_tuning), vp]
+    lib.ptored_reduce_scatter_ring.restype = i32
+    lib.ptored_accumulate_add.argtypes = [ctypes.POINTER(vp), i32, vp, i64, i64, i64, i64, i64,
+                                          i32, ctypes.POINTER(ptored_tuning), vp]
+    lib.ptored_accumulate_add.restype = i32
     lib.ptored_status_string.argtypes = [i32]
     lib.ptored_status_string.restype = ctypes.c_char_p
     lib.ptored_abi_version.restype = i32
@@ -114,6 +127,36 @@ def ptored_treduce_plan(srcs: Sequence[int], nranks: int, root: int, dst: int, r
     st = load().ptored_treduce_plan(_ptrs(srcs), nranks, root, dst, rows, cols, ld, valid_rows,
                                     valid_cols, dtype, op, t, ctypes.byref(info))
     return st, info
+
+
+def ptored_allreduce(bufs: Sequence[int], nranks: int, root: int, rows: int, cols: int, ld: int,
+                     valid_rows: int, valid_cols: int, dtype: int, op: int,
+                     tuning: Optional[ptored_tuning], stream: int) -> int:
+    t = ctypes.byref(tuning) if tuning is not None else None
+    return load().ptored_allreduce(_ptrs(bufs), nranks, root, rows, cols, ld, valid_rows,
+                                   valid_cols, dtype, op, t, stream)
+
+
+def ptored_ring_bounds(count: int, nranks: int, dtype: int) -> Tuple[int, list]:
+    out = (ctypes.c_int64 * (max(nranks, 0) + 1))()
+    st = load().ptored_ring_bounds(count, nranks, dtype, out)
+    return st, list(out)
+
+
+def ptored_reduce_scatter_ring(srcs: Sequence[int], nranks: int, dsts: Sequence[int], count: int,
+                               dtype: int, op: int, tuning: Optional[ptored_tuning],
+                               stream: int) -> int:
+    t = ctypes.byref(tuning) if tuning is not None else None
+    return load().ptored_reduce_scatter_ring(_ptrs(srcs), nranks, _ptrs(dsts), count, dtype, op,
+                                             t, stream)
+
+
+def ptored_accumulate_add(srcs: Sequence[int], nranks: int, dst: int, rows: int, cols: int,
+                          ld: int, valid_rows: int, valid_cols: int, dtype: int,
+                          tuning: Optional[ptored_tuning], stream: int) -> int:
+    t = ctypes.byref(tuning) if tuning is not None else None
+    return load().ptored_accumulate_add(_ptrs(srcs), nranks, dst, rows, cols, ld, valid_rows,
+                                        valid_cols, dtype, t, stream)
 
 
 def ptored_status_string(status: int) -> str:

@@ -1,0 +1,110 @@
+// accumulate_kernels.cuh -- push-with-add: dst += src_r for every rank r.
+//
+// Source: "Distributed Operators (N6)", PyPTO docs, pld.tile.remote_store /
+// pld.tensor.put with atomic = AtomicType.kAdd: a push that adds into the
+// peer's slice instead of overwriting it (the combine an all-to-all needs),
+// for fp32 / bf16 / fp16 / int32 among others.  With N ranks pushing into one
+// slice the contributions land in an unspecified order; on one GPU the N
+// pushes are the N source buffers and the slice is dst.
+//
+// Each workgroup pushes one rank's tile (blockIdx.y = rank): a 16-byte slot
+// is loaded from that rank's buffer and added into dst with one device-scope
+// atomic per 32-bit word (global_atomic_add_f32, global_atomic_pk_add_f16,
+// global_atomic_pk_add_bf16, global_atomic_add_u32).  A 16-bit element that
+// does not fill its 32-bit word (row remainders, the element-wise path) is
+// added with a compare-and-swap loop on the containing word that rewrites
+// only its own half, so the neighbouring half keeps its bits exactly.  The
+// order in which ranks' additions land differs from run to run, so float
+// results agree with any fixed order only to within the rounding of N
+// additions; i32 additions wrap and are exact.
+#pragma once
+
+#include "treduce_kernels.cuh"
+
+namespace ptored {
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ void atomic_add_word(char* p, uint32_t bits) {
+    if constexpr (DT == PTORED_F32) {
+        __hip_atomic_fetch_add(reinterpret_cast<float*>(p), as_f(bits), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (DT == PTORED_I32) {
+        __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(p), bits, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (DT == PTORED_F16) {
+        __builtin_amdgcn_global_atomic_fadd_v2f16((__attribute__((address_space(1))) h2*)p,
+                                                  as_h2(bits));
+    } else {
+        __builtin_amdgcn_global_atomic_fadd_v2bf16((__attribute__((address_space(1))) s16x2*)p,
+                                                   __builtin_bit_cast(s16x2, bits));
+    }
+}
+
+// a + b for one 16-bit element, rounded to the element type.
+template <int DT>
+__device__ __forceinline__ uint32_t add16(uint32_t a, uint32_t b) {
+    if constexpr (DT == PTORED_F16) {
+        return as_u(as_h2(a) + as_h2(b)) & 0xFFFFu;
+    } else {
+        return bf_pack_rne(bf_lo(a) + bf_lo(b), 0.0f) & 0xFFFFu;
+    }
+}
+
+// Add one element at p (ES bytes) atomically.
+template <int DT, int ES>
+__device__ __forceinline__ void atomic_add_elem(char* p, uint32_t bits) {
+    if constexpr (ES == 4) {
+        atomic_add_word<DT>(p, bits);
+    } else {
+        const uintptr_t addr = reinterpret_cast<uintptr_t>(p);
+        uint32_t* w = reinterpret_cast<uint32_t*>(addr & ~uintptr_t(3));
+        const uint32_t shift = (addr & 2u) ? 16u : 0u;
+        uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (;;) {
+            const uint32_t sum = add16<DT>((old >> shift) & 0xFFFFu, bits & 0xFFFFu);
+            const uint32_t desired = (old & ~(0xFFFFu << shift)) | (sum << shift);
+            if (__hip_atomic_compare_exchange_strong(w, &old, desired, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                break;
+        }
+    }
+}
+
+// Tiles as in treduce_kernel (U = 1): main tiles of 16-byte slots, then row
+// remainders; without VEC, element tiles only.  gridDim.y = N.
+template <int DT, int ES, int WALK, bool VEC>
+__global__ __launch_bounds__(kBlock) void accumulate_kernel(const KArgs a) {
+    const rsrc_t rs = make_rsrc(a.src[blockIdx.y], a.extent);
+    char* const d = static_cast<char*>(a.dst);
+    for (uint32_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+        if constexpr (VEC) {
+            if (t < a.main_tiles) {
+                const uint32_t off = slot_offset<WALK>(a, t * (uint32_t)kBlock + threadIdx.x);
+                if (off != kOutOfRange) {
+                    const u32x4 x = load16(rs, off);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) atomic_add_word<DT>(d + off + 4 * w, x[w]);
+                }
+            } else {
+                const uint32_t q = (t - a.main_tiles) * (uint32_t)kBlock + threadIdx.x;
+                if (q < a.ntail) {
+                    const uint32_t off = q * a.ld_bytes + a.tail_col_bytes;
+                    for (uint32_t e = 0; e < a.tail_bytes; e += ES)
+                        atomic_add_elem<DT, ES>(d + off + e, load_elem<ES>(rs, off + e));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kElemUnroll; ++u) {
+                const uint32_t q = t * (uint32_t)(kBlock * kElemUnroll) + (uint32_t)(u * kBlock) +
+                                   threadIdx.x;
+                const uint32_t off = tail_offset<WALK, ES>(a, q);
+                if (off != kOutOfRange) atomic_add_elem<DT, ES>(d + off, load_elem<ES>(rs, off));
+            }
+        }
+    }
+}
+
+}  // namespace ptored

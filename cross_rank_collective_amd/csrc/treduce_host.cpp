@@ -1,4 +1,5 @@
-// treduce_host.cpp -- C ABI of the N-way reduction: validation, plan, launch.
+// treduce_host.cpp -- C ABI of the N-way reduction and its collective
+// variants: validation, plan, launch.
 //
 // Sources (cited by title and section):
 //   [TREDUCE]  "CANN PTO-ISA TREDUCE instruction explained" (lpnh.cn article
@@ -7,7 +8,9 @@
 //              returns at once; data that fits takes the simple path, else
 //              the chunked walk), §4.3 fold order and the single-rank copy.
 //   [N6]       "Distributed Operators (N6)", PyPTO docs: append-only ABI
-//              enums; pld.tensor.allreduce works in place on the window.
+//              enums; pld.tensor.allreduce works in place on the window,
+//              its ring mode cuts the stream into per-rank segments;
+//              pld.tensor.put / remote_store with atomic = kAdd push-adds.
 //
 // Every argument check runs before the first HIP call, so every error status
 // is reachable without a GPU.
@@ -34,14 +37,15 @@ int64_t valid_span_bytes(int64_t vr, int64_t vc, int64_t ld, int es) {
     return ((vr - 1) * ld + vc) * es;
 }
 
-int validate(const void* const* srcs, int nranks, int root, const void* dst, int64_t rows,
-             int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols, int dtype,
-             int op) {
+// Checks shared by every entry point: rank count, pointers, shape, codes,
+// element alignment ([TREDUCE] §3.3 group checks; a valid rectangle inside a
+// rows x cols view).  `ptrs` holds every buffer the call touches.
+int validate_common(const void* const* ptrs, int nptrs, int nranks, int64_t rows, int64_t cols,
+                    int64_t ld, int64_t valid_rows, int64_t valid_cols, int dtype, int op) {
     if (nranks < 1 || nranks > PTORED_MAX_RANKS) return PTORED_ERR_INVALID_ARG;
-    if (root < 0 || root >= nranks) return PTORED_ERR_INVALID_ARG;
-    if (srcs == nullptr || dst == nullptr) return PTORED_ERR_INVALID_ARG;
-    for (int r = 0; r < nranks; ++r)
-        if (srcs[r] == nullptr) return PTORED_ERR_INVALID_ARG;
+    if (ptrs == nullptr) return PTORED_ERR_INVALID_ARG;
+    for (int r = 0; r < nptrs; ++r)
+        if (ptrs[r] == nullptr) return PTORED_ERR_INVALID_ARG;
     if (rows < 0 || cols < 0 || ld < 0 || valid_rows < 0 || valid_cols < 0)
         return PTORED_ERR_INVALID_ARG;
     if (cols > ld || valid_rows > rows || valid_cols > cols) return PTORED_ERR_INVALID_ARG;
@@ -50,34 +54,39 @@ int validate(const void* const* srcs, int nranks, int root, const void* dst, int
     if (op < PTORED_SUM || op > PTORED_PROD) return PTORED_ERR_UNSUPPORTED;
     // Every pointer holds whole elements (natural alignment of the type).
     const uintptr_t amask = (uintptr_t)esize_of(dtype) - 1u;
-    if ((reinterpret_cast<uintptr_t>(dst) & amask) != 0) return PTORED_ERR_INVALID_ARG;
-    for (int r = 0; r < nranks; ++r)
-        if ((reinterpret_cast<uintptr_t>(srcs[r]) & amask) != 0) return PTORED_ERR_INVALID_ARG;
-    // dst may be exactly a source (in place: each element is read by the one
-    // thread that later writes it); any other overlap is a race.
-    const int es = esize_of(dtype);
-    const int64_t span = valid_span_bytes(valid_rows, valid_cols, ld, es);
-    if (span > 0) {
-        const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst);
-        for (int r = 0; r < nranks; ++r) {
-            const uintptr_t s0 = reinterpret_cast<uintptr_t>(srcs[r]);
-            if (s0 == d0) continue;
-            if (s0 < d0 + (uintptr_t)span && d0 < s0 + (uintptr_t)span) return PTORED_ERR_OVERLAP;
+    for (int r = 0; r < nptrs; ++r)
+        if ((reinterpret_cast<uintptr_t>(ptrs[r]) & amask) != 0) return PTORED_ERR_INVALID_ARG;
+    return PTORED_OK;
+}
+
+bool spans_overlap(const void* a, const void* b, int64_t span) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)span && y < x + (uintptr_t)span;
+}
+
+// Every pair of buffers is either the same buffer (when `alias_ok`) or
+// disjoint over the `span` bytes the call touches.
+int check_pairs(const void* const* a, int na, const void* const* b, int nb, int64_t span,
+                bool alias_ok) {
+    if (span <= 0) return PTORED_OK;
+    for (int i = 0; i < na; ++i)
+        for (int j = 0; j < nb; ++j) {
+            if (a[i] == b[j] && alias_ok) continue;
+            if (spans_overlap(a[i], b[j], span)) return PTORED_ERR_OVERLAP;
         }
-    }
     return PTORED_OK;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Choose the kernel family and the slot geometry ([TREDUCE] §4.1 analog).
-int make_plan(const void* const* srcs, int nranks, int root, const void* dst, int64_t rows,
-              int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols, int dtype,
-              int op, const ptored_tuning* tuning, Plan& p) {
-    (void)root;
-    const int st = validate(srcs, nranks, root, dst, rows, cols, ld, valid_rows, valid_cols,
-                            dtype, op);
-    if (st != PTORED_OK) return st;
+enum Mode { kModeReduce, kModeAllreduce, kModeAccumulate };
+
+// Choose the kernel family and the slot geometry ([TREDUCE] §4.1 analog) for
+// already validated arguments.  `ptrs` holds every buffer the kernels touch
+// (all sources, and dst when there is one).
+int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows,
+              int64_t valid_cols, int64_t ld, int dtype, int op, const ptored_tuning* tuning,
+              Mode mode, Plan& p) {
     const uint32_t flags = tuning ? tuning->flags : 0u;
     p = Plan{};
     p.dtype = dtype;
@@ -88,6 +97,8 @@ int make_plan(const void* const* srcs, int nranks, int root, const void* dst, in
     p.valid_cols = valid_cols;
     p.ld = ld;
     p.xcd_remap = (flags & PTORED_NO_XCD_REMAP) == 0;
+    p.store_all = mode == kModeAllreduce;
+    p.accumulate = mode == kModeAccumulate;
     p.blocks_per_cu = tuning ? tuning->blocks_per_cu : 0;
     int64_t mlb = (tuning && tuning->max_launch_bytes > 0) ? tuning->max_launch_bytes
                                                            : kDefaultLaunchBytes;
@@ -106,13 +117,16 @@ int make_plan(const void* const* srcs, int nranks, int root, const void* dst, in
     p.rows_mode = contiguous ? 0 : 1;
     p.total_elems = contiguous ? (valid_rows == 1 ? valid_cols : valid_rows * ld) : 0;
 
-    bool use_vec = (flags & PTORED_FORCE_ELEMENTWISE) == 0 && aligned16(dst);
-    for (int r = 0; r < nranks && use_vec; ++r) use_vec = aligned16(srcs[r]);
+    bool use_vec = (flags & PTORED_FORCE_ELEMENTWISE) == 0;
+    for (int r = 0; r < nptrs && use_vec; ++r) use_vec = aligned16(ptrs[r]);
     if (use_vec && p.rows_mode && ((ld * p.esize) & 15) != 0) use_vec = false;
 
     if (use_vec) {
         p.vec_elems = 16 / p.esize;
-        if (nranks == 1) {
+        if (mode == kModeAccumulate) {
+            p.family = kFamVecRuntime;  // one source per workgroup row; U = 1
+            p.unroll = 1;
+        } else if (nranks == 1) {
             p.family = kFamCopy;
             p.unroll = unroll_for(1);
         } else if (nranks <= 16 && (flags & PTORED_FORCE_RUNTIME_N) == 0) {
@@ -137,7 +151,7 @@ int make_plan(const void* const* srcs, int nranks, int root, const void* dst, in
         // fetched twice), yet on MI355X the flattened walk measured faster
         // on ragged rows, so it stays the default.
         p.rows_mode = kWalkFlat;
-        if (p.family != kFamElem && (flags & PTORED_ROW_TILES) != 0) {
+        if (p.family != kFamElem && mode == kModeReduce && (flags & PTORED_ROW_TILES) != 0) {
             const int64_t full = valid_cols / vec;
             const int64_t per_tile = (int64_t)kBlock * p.unroll;
             const int64_t tiles = (full + per_tile - 1) / per_tile;
@@ -293,16 +307,19 @@ int cu_count_of_current_device(int& cu) {
     return PTORED_OK;
 }
 
-int run(const Plan& p, const void* const* srcs, int root, void* dst, hipStream_t stream) {
-    if (p.family == kFamNone) return PTORED_OK;
-    // Fold order of [TREDUCE] §4.3: the root's buffer first, then every
-    // other rank in ascending order.
-    const char* ordered[PTORED_MAX_RANKS];
+// Fold order of [TREDUCE] §4.3: the root's buffer first, then every other
+// rank in ascending order.
+void root_first_order(const void* const* srcs, int nranks, int root, const char** ordered) {
     ordered[0] = static_cast<const char*>(srcs[root]);
     int k = 1;
-    for (int r = 0; r < p.nranks; ++r)
+    for (int r = 0; r < nranks; ++r)
         if (r != root) ordered[k++] = static_cast<const char*>(srcs[r]);
+}
 
+// Launch the plan over buffers given in fold order (the kernels fold
+// ordered[0], ordered[1], ... in index order).
+int run(const Plan& p, const char* const* ordered, void* dst, hipStream_t stream) {
+    if (p.family == kFamNone) return PTORED_OK;
     int cu = 0;
     int st = cu_count_of_current_device(cu);
     if (st != PTORED_OK) return st;
@@ -339,6 +356,42 @@ int run(const Plan& p, const void* const* srcs, int root, void* dst, hipStream_t
     return PTORED_OK;
 }
 
+// TREDUCE arguments: validate, then plan.  ptrs = sources then dst.
+int plan_treduce(const void* const* srcs, int nranks, int root, const void* dst, int64_t rows,
+                 int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols, int dtype,
+                 int op, const ptored_tuning* tuning, Plan& p) {
+    if (nranks < 1 || nranks > PTORED_MAX_RANKS) return PTORED_ERR_INVALID_ARG;
+    if (root < 0 || root >= nranks) return PTORED_ERR_INVALID_ARG;
+    if (srcs == nullptr || dst == nullptr) return PTORED_ERR_INVALID_ARG;
+    const void* ptrs[PTORED_MAX_RANKS + 1];
+    for (int r = 0; r < nranks; ++r) ptrs[r] = srcs[r];
+    ptrs[nranks] = dst;
+    int st = validate_common(ptrs, nranks + 1, nranks, rows, cols, ld, valid_rows, valid_cols,
+                             dtype, op);
+    if (st != PTORED_OK) return st;
+    // dst may be exactly a source (in place: each element is read by the one
+    // thread that later writes it); any other overlap is a race.
+    const int64_t span = valid_span_bytes(valid_rows, valid_cols, ld, esize_of(dtype));
+    st = check_pairs(&ptrs[nranks], 1, ptrs, nranks, span, true);
+    if (st != PTORED_OK) return st;
+    return make_plan(ptrs, nranks + 1, nranks, valid_rows, valid_cols, ld, dtype, op, tuning,
+                     kModeReduce, p);
+}
+
+// Segment boundaries of the ring schedule ([N6] pld.tensor.allreduce, ring
+// mode): balanced floor(i * count / N); for 2-byte elements each interior
+// boundary rounded up to 16 elements (32 bytes) and capped at count.
+void ring_bounds(int64_t count, int nranks, int dtype, int64_t* bounds) {
+    bounds[0] = 0;
+    for (int i = 1; i < nranks; ++i) {
+        // i * count fits: count < 2^60 / 64 is checked by the callers
+        int64_t b = (int64_t)(((unsigned __int128)i * (uint64_t)count) / (uint64_t)nranks);
+        if (esize_of(dtype) == 2) b = std::min<int64_t>(count, (b + 15) / 16 * 16);
+        bounds[i] = b;
+    }
+    bounds[nranks] = count;
+}
+
 }  // namespace
 }  // namespace ptored
 
@@ -349,10 +402,12 @@ extern "C" int ptored_treduce_ex(const void* const* srcs, int nranks, int root, 
                                  int64_t valid_cols, int dtype, int op,
                                  const ptored_tuning* tuning, hipStream_t stream) {
     Plan p;
-    const int st = make_plan(srcs, nranks, root, dst, rows, cols, ld, valid_rows, valid_cols,
-                             dtype, op, tuning, p);
+    const int st = plan_treduce(srcs, nranks, root, dst, rows, cols, ld, valid_rows, valid_cols,
+                                dtype, op, tuning, p);
     if (st != PTORED_OK) return st;
-    return run(p, srcs, root, dst, stream);
+    const char* ordered[PTORED_MAX_RANKS];
+    root_first_order(srcs, nranks, root, ordered);
+    return run(p, ordered, dst, stream);
 }
 
 extern "C" int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst,
@@ -367,8 +422,8 @@ extern "C" int ptored_treduce_plan(const void* const* srcs, int nranks, int root
                                    int64_t valid_rows, int64_t valid_cols, int dtype, int op,
                                    const ptored_tuning* tuning, ptored_plan_info* info) {
     Plan p;
-    const int st = make_plan(srcs, nranks, root, dst, rows, cols, ld, valid_rows, valid_cols,
-                             dtype, op, tuning, p);
+    const int st = plan_treduce(srcs, nranks, root, dst, rows, cols, ld, valid_rows, valid_cols,
+                                dtype, op, tuning, p);
     if (st != PTORED_OK) return st;
     if (info) {
         info->path = p.family;
@@ -381,12 +436,120 @@ extern "C" int ptored_treduce_plan(const void* const* srcs, int nranks, int root
     return PTORED_OK;
 }
 
+extern "C" int ptored_allreduce(void* const* bufs, int nranks, int root, int64_t rows,
+                                int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
+                                int dtype, int op, const ptored_tuning* tuning,
+                                hipStream_t stream) {
+    if (nranks < 1 || nranks > PTORED_MAX_RANKS) return PTORED_ERR_INVALID_ARG;
+    if (root < 0 || root >= nranks) return PTORED_ERR_INVALID_ARG;
+    if (bufs == nullptr) return PTORED_ERR_INVALID_ARG;
+    const void* const* ptrs = bufs;
+    int st = validate_common(ptrs, nranks, nranks, rows, cols, ld, valid_rows, valid_cols, dtype,
+                             op);
+    if (st != PTORED_OK) return st;
+    const int64_t span = valid_span_bytes(valid_rows, valid_cols, ld, esize_of(dtype));
+    for (int i = 0; i < nranks; ++i) {  // pairwise: the same buffer or disjoint
+        st = check_pairs(&ptrs[i], 1, &ptrs[i + 1], nranks - 1 - i, span, true);
+        if (st != PTORED_OK) return st;
+    }
+    if (nranks == 1) return PTORED_OK;  // the fold of one buffer is itself
+    Plan p;
+    st = make_plan(ptrs, nranks, nranks, valid_rows, valid_cols, ld, dtype, op, tuning,
+                   kModeAllreduce, p);
+    if (st != PTORED_OK) return st;
+    const char* ordered[PTORED_MAX_RANKS];
+    root_first_order(ptrs, nranks, root, ordered);
+    return run(p, ordered, bufs[0], stream);
+}
+
+extern "C" int ptored_ring_bounds(int64_t count, int nranks, int dtype, int64_t* bounds) {
+    if (nranks < 1 || nranks > PTORED_MAX_RANKS || count < 0 || count > kMaxElems ||
+        bounds == nullptr)
+        return PTORED_ERR_INVALID_ARG;
+    if (dtype < PTORED_F32 || dtype > PTORED_I32) return PTORED_ERR_UNSUPPORTED;
+    ring_bounds(count, nranks, dtype, bounds);
+    return PTORED_OK;
+}
+
+extern "C" int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, void* const* dsts,
+                                          int64_t count, int dtype, int op,
+                                          const ptored_tuning* tuning, hipStream_t stream) {
+    if (nranks < 1 || nranks > PTORED_MAX_RANKS) return PTORED_ERR_INVALID_ARG;
+    if (srcs == nullptr || dsts == nullptr) return PTORED_ERR_INVALID_ARG;
+    if (count < 0 || count > kMaxElems) return PTORED_ERR_INVALID_ARG;
+    const void* ptrs[2 * PTORED_MAX_RANKS];
+    for (int r = 0; r < nranks; ++r) {
+        ptrs[r] = srcs[r];
+        ptrs[nranks + r] = dsts[r];
+    }
+    int st = validate_common(ptrs, 2 * nranks, nranks, 1, count, count, 1, count, dtype, op);
+    if (st != PTORED_OK) return st;
+    // Each dst is the same buffer as a source or as another dst, or disjoint
+    // from all of them: segments are disjoint, and each element is read and
+    // written by one thread of one launch.
+    const int64_t span = count * esize_of(dtype);
+    st = check_pairs(&ptrs[nranks], nranks, ptrs, nranks, span, true);
+    if (st != PTORED_OK) return st;
+    for (int i = 0; i < nranks; ++i) {
+        st = check_pairs(&ptrs[nranks + i], 1, &ptrs[nranks + i + 1], nranks - 1 - i, span, true);
+        if (st != PTORED_OK) return st;
+    }
+    int64_t bounds[PTORED_MAX_RANKS + 1];
+    ring_bounds(count, nranks, dtype, bounds);
+    const int es = esize_of(dtype);
+    for (int s = 0; s < nranks; ++s) {
+        const int64_t lo = bounds[s], len = bounds[s + 1] - bounds[s];
+        if (len == 0) continue;
+        // Ring fold order of segment s: ranks s+1, s+2, ..., s (mod N).
+        const char* ordered[PTORED_MAX_RANKS];
+        const void* seg[PTORED_MAX_RANKS + 1];
+        for (int k = 0; k < nranks; ++k) {
+            ordered[k] = static_cast<const char*>(srcs[(s + 1 + k) % nranks]) + lo * es;
+            seg[k] = ordered[k];
+        }
+        char* d = static_cast<char*>(dsts[s]) + lo * es;
+        seg[nranks] = d;
+        Plan p;
+        st = make_plan(seg, nranks + 1, nranks, 1, len, len, dtype, op, tuning, kModeReduce, p);
+        if (st != PTORED_OK) return st;
+        st = run(p, ordered, d, stream);
+        if (st != PTORED_OK) return st;
+    }
+    return PTORED_OK;
+}
+
+extern "C" int ptored_accumulate_add(const void* const* srcs, int nranks, void* dst,
+                                     int64_t rows, int64_t cols, int64_t ld, int64_t valid_rows,
+                                     int64_t valid_cols, int dtype, const ptored_tuning* tuning,
+                                     hipStream_t stream) {
+    if (nranks < 1 || nranks > PTORED_MAX_RANKS) return PTORED_ERR_INVALID_ARG;
+    if (srcs == nullptr || dst == nullptr) return PTORED_ERR_INVALID_ARG;
+    const void* ptrs[PTORED_MAX_RANKS + 1];
+    for (int r = 0; r < nranks; ++r) ptrs[r] = srcs[r];
+    ptrs[nranks] = dst;
+    int st = validate_common(ptrs, nranks + 1, nranks, rows, cols, ld, valid_rows, valid_cols,
+                             dtype, PTORED_SUM);
+    if (st != PTORED_OK) return st;
+    // dst may not be any source, not even exactly: a source read while other
+    // ranks' additions land in it would race.
+    const int64_t span = valid_span_bytes(valid_rows, valid_cols, ld, esize_of(dtype));
+    st = check_pairs(&ptrs[nranks], 1, ptrs, nranks, span, false);
+    if (st != PTORED_OK) return st;
+    Plan p;
+    st = make_plan(ptrs, nranks + 1, nranks, valid_rows, valid_cols, ld, dtype, PTORED_SUM,
+                   tuning, kModeAccumulate, p);
+    if (st != PTORED_OK) return st;
+    const char* ordered[PTORED_MAX_RANKS];
+    for (int r = 0; r < nranks; ++r) ordered[r] = static_cast<const char*>(srcs[r]);
+    return run(p, ordered, dst, stream);
+}
+
 extern "C" const char* ptored_status_string(int status) {
     switch (status) {
     case PTORED_OK: return "PTORED_OK";
     case PTORED_ERR_INVALID_ARG: return "PTORED_ERR_INVALID_ARG: bad rank count, root, pointer or shape";
     case PTORED_ERR_UNSUPPORTED: return "PTORED_ERR_UNSUPPORTED: unknown dtype or op";
-    case PTORED_ERR_OVERLAP: return "PTORED_ERR_OVERLAP: dst partially overlaps a source";
+    case PTORED_ERR_OVERLAP: return "PTORED_ERR_OVERLAP: buffers overlap in a way the call cannot allow";
     case PTORED_ERR_HIP: return "PTORED_ERR_HIP: the HIP runtime reported an error";
     default: return "unknown ptored status";
     }

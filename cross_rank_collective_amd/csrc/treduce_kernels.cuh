@@ -419,6 +419,19 @@ __device__ __forceinline__ uint32_t tail_offset(const KArgs& a, uint32_t q) {
     }
 }
 
+// Store one finished slot: to dst, or -- the in-place allreduce of [N6]
+// pld.tensor.allreduce -- back into every source buffer.  Each slot is read
+// from every buffer by the thread that later writes it, so the in-place
+// write never races a read.
+template <bool ALL>
+__device__ __forceinline__ void store_result(const KArgs& a, rsrc_t rd, uint32_t off, u32x4 v) {
+    if constexpr (ALL) {
+        for (uint32_t k = 0; k < a.nranks; ++k) store16(make_rsrc(a.src[k], a.extent), off, v);
+    } else {
+        store16(rd, off, v);
+    }
+}
+
 // Fold of one word from NR (compile-time) loaded values, in order.
 template <int DT, int OP, int NR, int U>
 __device__ __forceinline__ uint32_t fold_word(const u32x4 (&x)[NR][U], int u, int w) {
@@ -435,7 +448,7 @@ __device__ __forceinline__ uint32_t fold_word(const u32x4 (&x)[NR][U], int u, in
 // the scalar unit), so every wave's 1 KiB run starts 1 KiB into a row and
 // never shares a cache line with another wave; flattened walks number the
 // slots straight through.
-template <int DT, int OP, int NR, int U, int WALK>
+template <int DT, int OP, int NR, int U, int WALK, bool ALL>
 __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t in_tile = wave * (uint32_t)(64 * U) + lane;
@@ -468,7 +481,7 @@ __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
             u32x4 out;
 #pragma unroll
             for (int w = 0; w < 4; ++w) out[w] = fold_word<DT, OP, NR, U>(x, u, w);
-            store16(rd, off[u], out);
+            store_result<ALL>(a, rd, off[u], out);
         }
     } else {
         // Runtime rank count: groups of four sources in flight, then the
@@ -514,14 +527,14 @@ __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
             u32x4 out;
 #pragma unroll
             for (int w = 0; w < 4; ++w) out[w] = acc[u][w].get();
-            store16(rd, off[u], out);
+            store_result<ALL>(a, rd, off[u], out);
         }
     }
 }
 
 // One tail tile of the element-wise path: kElemUnroll elements per thread,
 // element by element.
-template <int DT, int OP, int ES, int NR, int WALK>
+template <int DT, int OP, int ES, int NR, int WALK, bool ALL>
 __device__ __forceinline__ void element_tile(const KArgs& a, uint32_t t) {
     constexpr int TU = kElemUnroll;
     const uint32_t base = t * (uint32_t)(kBlock * TU) + threadIdx.x;
@@ -545,13 +558,20 @@ __device__ __forceinline__ void element_tile(const KArgs& a, uint32_t t) {
         for (int u = 0; u < TU; ++u) acc[u].add(x[u]);
     }
 #pragma unroll
-    for (int u = 0; u < TU; ++u) store_elem<ES>(rd, off[u], acc[u].get());
+    for (int u = 0; u < TU; ++u) {
+        if constexpr (ALL) {
+            for (uint32_t k = 0; k < n; ++k)
+                store_elem<ES>(make_rsrc(a.src[k], a.extent), off[u], acc[u].get());
+        } else {
+            store_elem<ES>(rd, off[u], acc[u].get());
+        }
+    }
 }
 
 // One row remainder of TB bytes (the pages' partial column chunk with a
 // dynamic valid extent): loaded from every source, folded lane-wise in the
 // same order as the main tiles, stored with the same two exact accesses.
-template <int DT, int OP, int NR, int TB>
+template <int DT, int OP, int NR, int TB, bool ALL>
 __device__ __forceinline__ void row_tail(const KArgs& a, uint32_t off) {
     const rsrc_t rd = make_rsrc(a.dst, a.extent);
     Acc<DT, OP> acc[4];
@@ -569,23 +589,27 @@ __device__ __forceinline__ void row_tail(const KArgs& a, uint32_t off) {
     u32x4 out;
 #pragma unroll
     for (int w = 0; w < 4; ++w) out[w] = acc[w].get();
-    store_partial<TB>(rd, off, out);
+    if constexpr (ALL) {
+        for (uint32_t k = 0; k < n; ++k) store_partial<TB>(make_rsrc(a.src[k], a.extent), off, out);
+    } else {
+        store_partial<TB>(rd, off, out);
+    }
 }
 
 // One tail tile of the vector path: kBlock row remainders, one per thread.
-template <int DT, int OP, int ES, int NR>
+template <int DT, int OP, int ES, int NR, bool ALL>
 __device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
     const uint32_t q = t * (uint32_t)kBlock + threadIdx.x;
     if (q >= a.ntail) return;
     const uint32_t off = q * a.ld_bytes + a.tail_col_bytes;
     switch (a.tail_bytes) {  // uniform over the launch
-    case 2: if constexpr (ES == 2) row_tail<DT, OP, NR, 2>(a, off); break;
-    case 4: row_tail<DT, OP, NR, 4>(a, off); break;
-    case 6: if constexpr (ES == 2) row_tail<DT, OP, NR, 6>(a, off); break;
-    case 8: row_tail<DT, OP, NR, 8>(a, off); break;
-    case 10: if constexpr (ES == 2) row_tail<DT, OP, NR, 10>(a, off); break;
-    case 12: row_tail<DT, OP, NR, 12>(a, off); break;
-    case 14: if constexpr (ES == 2) row_tail<DT, OP, NR, 14>(a, off); break;
+    case 2: if constexpr (ES == 2) row_tail<DT, OP, NR, 2, ALL>(a, off); break;
+    case 4: row_tail<DT, OP, NR, 4, ALL>(a, off); break;
+    case 6: if constexpr (ES == 2) row_tail<DT, OP, NR, 6, ALL>(a, off); break;
+    case 8: row_tail<DT, OP, NR, 8, ALL>(a, off); break;
+    case 10: if constexpr (ES == 2) row_tail<DT, OP, NR, 10, ALL>(a, off); break;
+    case 12: row_tail<DT, OP, NR, 12, ALL>(a, off); break;
+    case 14: if constexpr (ES == 2) row_tail<DT, OP, NR, 14, ALL>(a, off); break;
     default: break;
     }
 }
@@ -594,20 +618,21 @@ __device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
 // tail tiles; block b takes tiles b, b + G, ... (one tile per block when
 // G equals the tile count).  NR == 0: runtime rank count.  VEC: 16-byte
 // main tiles with row-remainder tails; otherwise element tiles only.
-// WALK: kWalkContig, kWalkRowTiles or kWalkFlat.
-template <int DT, int OP, int ES, int NR, int U, int WALK, bool VEC>
+// WALK: kWalkContig, kWalkRowTiles or kWalkFlat.  ALL: store the result
+// into every source buffer instead of dst (in-place allreduce).
+template <int DT, int OP, int ES, int NR, int U, int WALK, bool VEC, bool ALL>
 __global__ __launch_bounds__(kBlock) void treduce_kernel(const KArgs a) {
     const uint32_t grid = gridDim.x;
     for (uint32_t t = logical_block(blockIdx.x, grid, a.xcd_remap != 0u); t < a.total_tiles;
          t += grid) {
         if constexpr (VEC) {
             if (t < a.main_tiles) {
-                main_tile<DT, OP, NR, U, WALK>(a, t);
+                main_tile<DT, OP, NR, U, WALK, ALL>(a, t);
             } else {
-                row_tail_tile<DT, OP, ES, NR>(a, t - a.main_tiles);
+                row_tail_tile<DT, OP, ES, NR, ALL>(a, t - a.main_tiles);
             }
         } else {
-            element_tile<DT, OP, ES, NR, WALK>(a, t);
+            element_tile<DT, OP, ES, NR, WALK, ALL>(a, t);
         }
     }
 }

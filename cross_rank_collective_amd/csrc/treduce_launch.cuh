@@ -7,6 +7,7 @@
 // runtime rank loop.
 #pragma once
 
+#include "accumulate_kernels.cuh"
 #include "treduce_kernels.cuh"
 
 namespace ptored {
@@ -39,27 +40,27 @@ static void launch(const Plan& p, const KArgs& a, int cu_count, hipStream_t s) {
     hipLaunchKernelGGL(KERNEL, dim3((uint32_t)grid), dim3(kBlock), 0, s, a);
 }
 
-template <int DT, int OP, int ES, int WALK>
+template <int DT, int OP, int ES, int WALK, bool ALL>
 static int dispatch_n(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
     if (p.family == kFamElem) {
         if constexpr (WALK == kWalkRowTiles) {
             return -1;  // the element-wise path never takes row tiles
         } else {
-            launch<treduce_kernel<DT, OP, ES, 0, 1, WALK, false>>(p, a, cu, s);
+            launch<treduce_kernel<DT, OP, ES, 0, 1, WALK, false, ALL>>(p, a, cu, s);
             return 0;
         }
     }
     switch (p.family == kFamVecFixed ? p.nranks : 0) {
 #define PTORED_CASE(n)                                                                 \
     case n:                                                                            \
-        launch<treduce_kernel<DT, OP, ES, n, unroll_for(n), WALK, true>>(p, a, cu, s); \
+        launch<treduce_kernel<DT, OP, ES, n, unroll_for(n), WALK, true, ALL>>(p, a, cu, s); \
         return 0;
         PTORED_CASE(2) PTORED_CASE(3) PTORED_CASE(4) PTORED_CASE(5) PTORED_CASE(6)
         PTORED_CASE(7) PTORED_CASE(8) PTORED_CASE(9) PTORED_CASE(10) PTORED_CASE(11)
         PTORED_CASE(12) PTORED_CASE(13) PTORED_CASE(14) PTORED_CASE(15) PTORED_CASE(16)
 #undef PTORED_CASE
     case 0:
-        launch<treduce_kernel<DT, OP, ES, 0, kRuntimeUnroll, WALK, true>>(p, a, cu, s);
+        launch<treduce_kernel<DT, OP, ES, 0, kRuntimeUnroll, WALK, true, ALL>>(p, a, cu, s);
         return 0;
     default: return -1;
     }
@@ -67,10 +68,41 @@ static int dispatch_n(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
 
 template <int DT, int OP, int ES>
 static int dispatch_op(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
+    if (p.store_all) {  // in-place allreduce: contiguous or flattened walks only
+        switch (p.rows_mode) {
+        case kWalkContig: return dispatch_n<DT, OP, ES, kWalkContig, true>(p, a, cu, s);
+        case kWalkFlat: return dispatch_n<DT, OP, ES, kWalkFlat, true>(p, a, cu, s);
+        default: return -1;
+        }
+    }
     switch (p.rows_mode) {
-    case kWalkContig: return dispatch_n<DT, OP, ES, kWalkContig>(p, a, cu, s);
-    case kWalkRowTiles: return dispatch_n<DT, OP, ES, kWalkRowTiles>(p, a, cu, s);
-    default: return dispatch_n<DT, OP, ES, kWalkFlat>(p, a, cu, s);
+    case kWalkContig: return dispatch_n<DT, OP, ES, kWalkContig, false>(p, a, cu, s);
+    case kWalkRowTiles: return dispatch_n<DT, OP, ES, kWalkRowTiles, false>(p, a, cu, s);
+    default: return dispatch_n<DT, OP, ES, kWalkFlat, false>(p, a, cu, s);
+    }
+}
+
+// Push-with-add: a 2-D grid, one row of workgroups per rank.
+template <int DT, int ES, int WALK, bool VEC>
+static void launch_accumulate(const KArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((accumulate_kernel<DT, ES, WALK, VEC>),
+                       dim3(a.total_tiles > 0 ? a.total_tiles : 1, a.nranks), dim3(kBlock), 0, s,
+                       a);
+}
+
+template <int DT, int ES>
+static int dispatch_accumulate(const Plan& p, const KArgs& a, hipStream_t s) {
+    const bool vec = p.family != kFamElem;
+    switch (p.rows_mode) {
+    case kWalkContig:
+        if (vec) launch_accumulate<DT, ES, kWalkContig, true>(a, s);
+        else launch_accumulate<DT, ES, kWalkContig, false>(a, s);
+        return 0;
+    case kWalkFlat:
+        if (vec) launch_accumulate<DT, ES, kWalkFlat, true>(a, s);
+        else launch_accumulate<DT, ES, kWalkFlat, false>(a, s);
+        return 0;
+    default: return -1;
     }
 }
 
@@ -81,13 +113,13 @@ static int dispatch_copy(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
     constexpr int U = unroll_for(1);
     switch (p.rows_mode) {
     case kWalkContig:
-        launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkContig, true>>(p, a, cu, s);
+        launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkContig, true, false>>(p, a, cu, s);
         break;
     case kWalkRowTiles:
-        launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkRowTiles, true>>(p, a, cu, s);
+        launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkRowTiles, true, false>>(p, a, cu, s);
         break;
     default:
-        launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkFlat, true>>(p, a, cu, s);
+        launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkFlat, true, false>>(p, a, cu, s);
         break;
     }
     return 0;
@@ -95,6 +127,7 @@ static int dispatch_copy(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
 
 template <int DT, int ES>
 static int dispatch_dtype(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
+    if (p.accumulate) return dispatch_accumulate<DT, ES>(p, a, s);
     if (p.family == kFamCopy) return dispatch_copy<DT, ES>(p, a, cu, s);
     switch (p.op) {
     case PTORED_SUM: return dispatch_op<DT, PTORED_SUM, ES>(p, a, cu, s);

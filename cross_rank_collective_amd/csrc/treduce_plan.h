@@ -71,6 +71,8 @@ struct Plan {
     int vec_elems;      // elements per slot
     int unroll;         // slots per thread per main tile
     bool xcd_remap;
+    bool store_all;     // in-place allreduce: the result goes back into every source
+    bool accumulate;    // push-with-add: dst += every source, by atomics
     int blocks_per_cu;  // 0: one tile per block; > 0: persistent grid; < 0: at occupancy
     // geometry of the whole call
     int64_t valid_rows;

@@ -158,6 +158,67 @@ int ptored_treduce_plan(const void* const* srcs, int nranks, int root, const voi
                         int64_t valid_cols, int dtype, int op, const ptored_tuning* tuning,
                         ptored_plan_info* info);
 
+/*
+ * ptored_allreduce -- the in-place allreduce of one device's share
+ * ([N6] pld.tensor.allreduce: every participating rank's window slice is
+ * reduced in place).  Every buffer's valid rectangle is replaced by the fold
+ * of all N buffers (same fold order and arithmetic as ptored_treduce with
+ * the same root); everything outside the valid rectangle is left unchanged.
+ *
+ * bufs        HOST array of N DEVICE pointers, each read and written.  Two
+ *             entries may be the same buffer; partially overlapping buffers
+ *             are rejected (PTORED_ERR_OVERLAP).  N == 1 changes nothing.
+ * Other arguments and errors as ptored_treduce_ex (tuning may be NULL).
+ * Bytes moved: N reads and N writes of the valid rectangle.
+ */
+int ptored_allreduce(void* const* bufs, int nranks, int root, int64_t rows, int64_t cols,
+                     int64_t ld, int64_t valid_rows, int64_t valid_cols, int dtype, int op,
+                     const ptored_tuning* tuning, hipStream_t stream);
+
+/*
+ * ptored_ring_bounds -- segment boundaries of the ring schedule ([N6]
+ * pld.tensor.allreduce, ring mode): a stream of `count` elements is cut at
+ * floor(i * count / N); for 2-byte element types every interior boundary is
+ * then rounded up to a multiple of 16 elements (32 bytes) and capped at
+ * `count`, so short streams can have empty segments.  `bounds` (HOST, N + 1
+ * entries) receives 0, b_1, ..., b_{N-1}, count.  No HIP call.
+ */
+int ptored_ring_bounds(int64_t count, int nranks, int dtype, int64_t* bounds);
+
+/*
+ * ptored_reduce_scatter_ring -- the reduce-scatter half of the ring schedule
+ * on one device.  Segment s ([b_s, b_{s+1}) of ptored_ring_bounds) of the
+ * N source streams is folded in ring order -- ranks s+1, s+2, ..., s (mod N),
+ * the order in which a ring passes the partial result from rank s+1 round
+ * to its owner s -- and written to dsts[s] at the same element positions.
+ * Nothing else of any dst is written.
+ *
+ * srcs, dsts  HOST arrays of N DEVICE pointers to streams of `count`
+ *             elements.  dsts[s] may be srcs[s] (in place into the owner's
+ *             window), any other source or another dst; partial overlaps are
+ *             rejected.
+ * Errors as ptored_treduce_ex.  One launch per non-empty segment.
+ */
+int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, void* const* dsts,
+                               int64_t count, int dtype, int op, const ptored_tuning* tuning,
+                               hipStream_t stream);
+
+/*
+ * ptored_accumulate_add -- push-with-add into one slice ([N6]
+ * pld.tensor.put / remote_store with atomic = kAdd, the pushed data added
+ * into the peer's slice): dst[i, j] += src_0[i, j] + ... + src_{N-1}[i, j]
+ * over the valid rectangle, every source's contribution applied with
+ * device-scope atomic adds, so the additions land in an unspecified order
+ * (float results vary within the rounding of N additions; i32 wraps and is
+ * exact).  A 16-bit element that does not fill its aligned 32-bit word is
+ * added by a compare-and-swap on that word which rewrites only its own half.
+ * dst must be device memory of this GPU and must not overlap any source
+ * (not even exactly).  Other arguments and errors as ptored_treduce_ex.
+ */
+int ptored_accumulate_add(const void* const* srcs, int nranks, void* dst, int64_t rows,
+                          int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
+                          int dtype, const ptored_tuning* tuning, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* ptored_status_string(int status);
 

@@ -178,3 +178,37 @@ def test_workload_plans():
                      op=B.OPS[w.ops[0]])
         assert (B.PATHS[info.path], info.rows_mode) == want[name], name  # 2 = flattened
         assert info.launches == 1
+
+
+def test_ring_bounds_match_the_oracle_rule():
+    import oracle
+    rng = __import__("numpy").random.default_rng(4)
+    for _ in range(200):
+        count = int(rng.integers(0, 100000))
+        n = int(rng.integers(1, 65))
+        for dt, code in B.DTYPES.items():
+            st, b = crc.ptored_ring_bounds(count, n, code)
+            assert st == 0
+            assert b == list(oracle.ring_bounds(count, n, dt))
+    assert crc.ptored_ring_bounds(10, 0, 0)[0] == -1
+    assert crc.ptored_ring_bounds(-1, 2, 0)[0] == -1
+    assert crc.ptored_ring_bounds(10, 2, 7)[0] == -2
+
+
+def test_collective_argument_errors_before_any_hip_call():
+    lib = B
+    s = 0
+    # allreduce: bad root, partial overlap between buffers, misaligned pointer
+    assert lib.ptored_allreduce(A[:2], 2, 2, 4, 4, 4, 4, 4, 0, 0, None, s) == -1
+    assert lib.ptored_allreduce([A[0], A[0] + 8], 2, 0, 4, 4, 4, 4, 4, 0, 0, None, s) == -3
+    assert lib.ptored_allreduce([A[0], A[1] + 2], 2, 0, 4, 4, 4, 4, 4, 0, 0, None, s) == -1
+    assert lib.ptored_allreduce(A[:2], 2, 0, 4, 4, 4, 0, 4, 0, 0, None, s) == 0  # empty
+    assert lib.ptored_allreduce([A[0]], 1, 0, 4, 4, 4, 4, 4, 0, 0, None, s) == 0  # N == 1
+    # reduce-scatter: partial overlap of a dst with a source, bad op, empty stream
+    assert lib.ptored_reduce_scatter_ring(A[:2], 2, [A[2], A[0] + 16], 64, 0, 0, None, s) == -3
+    assert lib.ptored_reduce_scatter_ring(A[:2], 2, A[2:4], 64, 0, 9, None, s) == -2
+    assert lib.ptored_reduce_scatter_ring(A[:2], 2, A[2:4], 0, 0, 0, None, s) == 0
+    assert lib.ptored_reduce_scatter_ring(A[:2], 2, A[2:4], -1, 0, 0, None, s) == -1
+    # accumulate: dst may not alias a source, even exactly
+    assert lib.ptored_accumulate_add(A[:2], 2, A[1], 4, 4, 4, 4, 4, 0, None, s) == -3
+    assert lib.ptored_accumulate_add(A[:2], 2, D, 4, 4, 4, 0, 4, 0, None, s) == 0  # empty

@@ -1,0 +1,247 @@
+"""GPU parity of the collective variants through the C ABI: in-place
+allreduce, the ring reduce-scatter share, and push-with-add accumulation.
+
+Bar: bit-exact for the allreduce and the reduce-scatter (same fold order and
+arithmetic as the oracle); for push-with-add, bit-exact for i32, and for the
+float types within the rounding bound of N additions in any order (plus N
+times the smallest normal, in case the atomic unit flushes subnormal sums).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from cross_rank_collective_amd import binding as B
+from cross_rank_collective_amd import workloads as W
+from tests.gpu_helpers import DevBuf, ESIZE, compare, isnan_bits, bits, say, sentinel, valid_mask
+from tests.test_parity_gpu import _rand_elems
+
+pytestmark = pytest.mark.gpu
+
+DT = ["f32", "bf16", "f16", "i32"]
+OPS = ["sum", "max", "min", "prod"]
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _upload(arrs, offs, fill=0xA5):
+    out = []
+    for a, o in zip(arrs, offs):
+        b = DevBuf(a.size * a.itemsize, o, fill=fill)
+        b.upload(a)
+        out.append(b)
+    return out
+
+
+# ------------------------------------------------------------- allreduce ---
+
+@pytest.mark.parametrize("dtype", DT)
+def test_allreduce_in_place_random(dtype):
+    rng = np.random.default_rng({"f32": 31, "bf16": 32, "f16": 33, "i32": 34}[dtype])
+    es = ESIZE[dtype]
+    for case in range(24):
+        n = int(rng.choice([2, 3, 5, 8, 16, 17, 40]))
+        rows = int(rng.integers(1, 40))
+        cols = int(rng.integers(1, 600))
+        ld = cols + int(rng.choice([0, 0, 3, 8]))
+        vr, vc = int(rng.integers(1, rows + 1)), int(rng.integers(1, cols + 1))
+        root = int(rng.integers(0, n))
+        op = OPS[case % 4]
+        flags = [0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_FORCE_ROWS,
+                 B.PTORED_FORCE_RUNTIME_N][case % 4]
+        offs = [0 if case % 3 else int(rng.integers(0, 8)) * es for _ in range(n)]
+        size = (rows - 1) * ld + cols
+        srcs = [_rand_elems(dtype, rng, size, wild=0.05) for _ in range(n)]
+        bufs = _upload(srcs, offs)
+        say(f"allreduce#{case} {dtype} {op} N={n} root={root} {rows}x{cols} ld={ld} "
+            f"valid={vr}x{vc} flags={flags}")
+        st = B.ptored_allreduce([b.ptr for b in bufs], n, root, rows, cols, ld, vr, vc,
+                                B.DTYPES[dtype], B.OPS[op], B.tuning(flags=flags), _stream())
+        torch.cuda.synchronize()
+        assert st == 0, B.ptored_status_string(st)
+        want = [s.copy() for s in srcs]
+        oracle.allreduce_inplace(want, root=root, dtype=dtype, op=op, rows=rows, cols=cols,
+                                 ld=ld, valid_rows=vr, valid_cols=vc)
+        m = valid_mask(rows, ld, vr, vc, size)
+        for r, b in enumerate(bufs):
+            got = b.download(dtype)
+            assert compare(dtype, got[m], want[r][m]).all(), (case, r)
+            assert np.array_equal(got[~m].view(np.uint8), srcs[r][~m].view(np.uint8)), (case, r)
+            assert b.guards_intact()
+
+
+def test_allreduce_two_entries_same_buffer():
+    """The same buffer listed twice counts as two ranks and gets the result."""
+    rng = np.random.default_rng(35)
+    a = rng.standard_normal(4096).astype(np.float32)
+    c = rng.standard_normal(4096).astype(np.float32)
+    ba, bc = _upload([a, c], [0, 0])
+    st = B.ptored_allreduce([ba.ptr, bc.ptr, ba.ptr], 3, 0, 1, 4096, 4096, 1, 4096, 0, 0, None,
+                            _stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    want = [a.copy(), c.copy(), a.copy()]
+    oracle.allreduce_inplace(want, root=0, dtype="f32", op="sum", rows=1, cols=4096, ld=4096,
+                             valid_rows=1, valid_cols=4096)
+    assert np.array_equal(ba.download("f32"), want[0])
+    assert np.array_equal(bc.download("f32"), want[1])
+
+
+def test_allreduce_full_size_workload():
+    w = W.WORKLOADS["n16_i32_4096x4096"]
+    srcs = W.make_sources(w)
+    bufs = _upload(srcs, [0] * w.nranks)
+    say("allreduce full n16_i32_4096x4096 sum")
+    st = B.ptored_allreduce([b.ptr for b in bufs], w.nranks, 0, w.rows, w.cols, w.ld,
+                            w.valid_rows, w.valid_cols, 3, 0, None, _stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    want = np.sum(np.stack([s.astype(np.int64) for s in srcs]), axis=0)
+    want = ((want + 2**31) % 2**32 - 2**31).astype(np.int32)
+    for b in bufs:
+        assert np.array_equal(b.download("i32"), want)
+
+
+# ------------------------------------------------------ ring reduce-scatter ---
+
+@pytest.mark.parametrize("dtype", DT)
+def test_reduce_scatter_ring_random(dtype):
+    rng = np.random.default_rng({"f32": 41, "bf16": 42, "f16": 43, "i32": 44}[dtype])
+    for case in range(24):
+        n = int(rng.choice([1, 2, 3, 4, 7, 8, 16, 20]))
+        count = int(rng.choice([0, 1, 5, 20, 63, 1000, 4099, 70001]))
+        op = OPS[case % 4]
+        flags = [0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_FORCE_RUNTIME_N, 0][case % 4]
+        in_place = case % 3 == 0
+        srcs = [_rand_elems(dtype, rng, max(count, 1), wild=0.05) for _ in range(n)]
+        sb = _upload(srcs, [0] * n)
+        if in_place:
+            db = sb
+            d0 = [s.copy() for s in srcs]
+        else:
+            db = [DevBuf(max(count, 1) * ESIZE[dtype], 0, fill=0xFF) for _ in range(n)]
+            d0 = [sentinel(dtype, max(count, 1)) for _ in range(n)]
+        say(f"ring#{case} {dtype} {op} N={n} count={count} in_place={in_place} flags={flags}")
+        st = B.ptored_reduce_scatter_ring([b.ptr for b in sb], n, [b.ptr for b in db], count,
+                                          B.DTYPES[dtype], B.OPS[op], B.tuning(flags=flags),
+                                          _stream())
+        torch.cuda.synchronize()
+        assert st == 0, B.ptored_status_string(st)
+        want = [d.copy() for d in d0]
+        oracle.reduce_scatter_ring([s.copy() for s in srcs], want, count=count, dtype=dtype,
+                                   op=op)
+        for s in range(n):
+            got = db[s].download(dtype)
+            assert compare(dtype, got, want[s]).all(), (case, s)
+            assert db[s].guards_intact()
+
+
+def test_reduce_scatter_ring_full_size_bf16():
+    w = W.WORKLOADS["n8_bf16_8192x8192"]
+    srcs = W.make_sources(w)
+    count = w.buffer_elems
+    sb = _upload(srcs, [0] * w.nranks)
+    say("ring full n8_bf16_8192x8192 sum in place")
+    st = B.ptored_reduce_scatter_ring([b.ptr for b in sb], w.nranks, [b.ptr for b in sb], count,
+                                      1, 0, None, _stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    bounds = oracle.ring_bounds(count, w.nranks, "bf16")
+    rng = np.random.default_rng(45)
+    for s in range(w.nranks):
+        got = sb[s].download("bf16")
+        # sampled windows of each segment, computed by the oracle one by one
+        for start in list(rng.integers(bounds[s], bounds[s + 1] - 4096, 3)) + [bounds[s],
+                                                                               bounds[s + 1] - 4096]:
+            lo, hi = int(start), int(start) + 4096
+            sub = [np.ascontiguousarray(x[lo:hi]) for x in srcs]
+            ring = [sub[(s + 1 + k) % w.nranks] for k in range(w.nranks)]
+            want = sentinel("bf16", hi - lo)
+            oracle.treduce(ring, want, root=0, dtype="bf16", op="sum", rows=1, cols=hi - lo,
+                           ld=hi - lo, valid_rows=1, valid_cols=hi - lo)
+            assert np.array_equal(got[lo:hi], want), (s, lo)
+        # outside its own segment rank s's window is untouched
+        outside = np.ones(count, bool)
+        outside[bounds[s]:bounds[s + 1]] = False
+        assert np.array_equal(got[outside], srcs[s][outside])
+
+
+# ------------------------------------------------------------ push-with-add ---
+
+UNIT = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+TINY = {"f32": 2.0 ** -126, "f16": 2.0 ** -14, "bf16": 2.0 ** -126}
+
+
+def _finite_values(dtype, rng, n):
+    v = (rng.standard_normal(n) * np.exp2(rng.integers(-4, 4, n))).astype(np.float32)
+    if dtype == "f32":
+        return v
+    if dtype == "i32":
+        return rng.integers(-2**30, 2**30, n, dtype=np.int64).astype(np.int32)
+    if dtype == "f16":
+        return v.astype(np.float16).view(np.uint16)
+    return torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_accumulate_add_random(dtype):
+    rng = np.random.default_rng({"f32": 51, "bf16": 52, "f16": 53, "i32": 54}[dtype])
+    es = ESIZE[dtype]
+    for case in range(16):
+        n = int(rng.choice([1, 2, 3, 8, 16, 33]))
+        rows = int(rng.integers(1, 30))
+        cols = int(rng.integers(1, 700))
+        ld = cols + int(rng.choice([0, 1, 8]))
+        vr, vc = int(rng.integers(1, rows + 1)), int(rng.integers(1, cols + 1))
+        flags = [0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_FORCE_ROWS][case % 3]
+        size = (rows - 1) * ld + cols
+        srcs = [_finite_values(dtype, rng, size) for _ in range(n)]
+        d0 = _finite_values(dtype, rng, size)
+        sb = _upload(srcs, [0 if case % 2 else int(rng.integers(0, 4)) * es for _ in range(n)])
+        db = _upload([d0], [0 if case % 4 else 2 * es])[0]
+        say(f"accumulate#{case} {dtype} N={n} {rows}x{cols} ld={ld} valid={vr}x{vc} "
+            f"flags={flags}")
+        st = B.ptored_accumulate_add([b.ptr for b in sb], n, db.ptr, rows, cols, ld, vr, vc,
+                                     B.DTYPES[dtype], B.tuning(flags=flags), _stream())
+        torch.cuda.synchronize()
+        assert st == 0, B.ptored_status_string(st)
+        got = db.download(dtype)
+        want = d0.copy()
+        exact, absum = oracle.accumulate_add(srcs, want, dtype=dtype, rows=rows, cols=cols,
+                                             ld=ld, valid_rows=vr, valid_cols=vc)
+        m = valid_mask(rows, ld, vr, vc, size)
+        assert np.array_equal(got[~m].view(np.uint8), d0[~m].view(np.uint8)), case
+        assert db.guards_intact()
+        if dtype == "i32":
+            # wrap-around integer sums have one possible result
+            assert compare(dtype, got[m], want[m]).all(), case
+        else:
+            g = oracle.to_double(dtype, bits(dtype, got[m]).astype(np.uint32))
+            bound = n * UNIT[dtype] * absum * 1.0001 + n * TINY[dtype]
+            assert np.all(np.abs(g - exact) <= bound), case
+
+
+def test_accumulate_add_full_size_i32_exact():
+    w = W.WORKLOADS["n16_i32_4096x4096"]
+    srcs = W.make_sources(w)
+    sb = _upload(srcs, [0] * w.nranks)
+    d0 = np.arange(w.buffer_elems, dtype=np.int32)
+    db = _upload([d0], [0])[0]
+    say("accumulate full n16_i32_4096x4096")
+    st = B.ptored_accumulate_add([b.ptr for b in sb], w.nranks, db.ptr, w.rows, w.cols, w.ld,
+                                 w.valid_rows, w.valid_cols, 3, None, _stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    want = d0.astype(np.int64) + np.sum(np.stack([s.astype(np.int64) for s in srcs]), axis=0)
+    want = ((want + 2**31) % 2**32 - 2**31).astype(np.int32)
+    assert np.array_equal(db.download("i32"), want)
