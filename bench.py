@@ -6,6 +6,14 @@ effective HBM GB/s = (N+1) * valid bytes / time, with the roofline of the
 reduce kernel and the CPU oracle timed on a bounded sample as a baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--op OP]
+                    [--mode treduce|allreduce|reduce_scatter_ring|accumulate_add]
+
+The default mode is the reduction itself (dst = fold of the N sources); the
+other modes time the collective variants on the same workload: the in-place
+allreduce (N reads + N writes per valid element), the ring reduce-scatter
+share over the whole buffer as one stream (N reads + 1 write per element)
+and push-with-add by atomics (N source reads + one read and one write of dst
+per element, the least any order of the additions must move).
 """
 
 from __future__ import annotations
@@ -187,6 +195,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--op", default=None)
+    ap.add_argument("--mode", default="treduce",
+                    choices=["treduce", "allreduce", "reduce_scatter_ring", "accumulate_add"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -221,11 +231,39 @@ def main() -> int:
     dst_t = torch.full((w.buffer_elems * w.esize,), 0xFF, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     ptrs = [t.data_ptr() for t in src_t]
+    dt, opc = B.DTYPES[w.dtype], B.OPS[op]
+    mode = args.mode
+    if mode == "treduce":
+        algo_bytes = w.algorithmic_bytes
+
+        def call():
+            return B.ptored_treduce(ptrs, w.nranks, w.root, dst_t.data_ptr(), w.rows, w.cols,
+                                    w.ld, w.valid_rows, w.valid_cols, dt, opc,
+                                    stream.cuda_stream)
+    elif mode == "allreduce":
+        algo_bytes = 2 * w.nranks * w.valid_bytes
+
+        def call():
+            return B.ptored_allreduce(ptrs, w.nranks, w.root, w.rows, w.cols, w.ld,
+                                      w.valid_rows, w.valid_cols, dt, opc, None,
+                                      stream.cuda_stream)
+    elif mode == "reduce_scatter_ring":
+        count = w.buffer_elems
+        algo_bytes = (w.nranks + 1) * count * w.esize
+
+        def call():  # in place: segment s goes back into rank s's buffer
+            return B.ptored_reduce_scatter_ring(ptrs, w.nranks, ptrs, count, dt, opc, None,
+                                                stream.cuda_stream)
+    else:
+        algo_bytes = (w.nranks + 2) * w.valid_bytes
+
+        def call():
+            return B.ptored_accumulate_add(ptrs, w.nranks, dst_t.data_ptr(), w.rows, w.cols,
+                                           w.ld, w.valid_rows, w.valid_cols, dt, None,
+                                           stream.cuda_stream)
 
     def step():
-        st = B.ptored_treduce(ptrs, w.nranks, w.root, dst_t.data_ptr(), w.rows, w.cols, w.ld,
-                              w.valid_rows, w.valid_cols, B.DTYPES[w.dtype], B.OPS[op],
-                              stream.cuda_stream)
+        st = call()
         if st != 0:
             raise RuntimeError(B.ptored_status_string(st))
 
@@ -241,11 +279,10 @@ def main() -> int:
     torch.cuda.synchronize(dev)
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    algo_bytes = w.algorithmic_bytes
     gbs = algo_bytes / (ms_step * 1e-3) / 1e9
     elems_s = w.valid_rows * w.valid_cols / (ms_step * 1e-3)
 
-    traffic = stored_traffic(name, op)
+    traffic = stored_traffic(name, op) if mode == "treduce" else None
     line = {
         "metric": "effective HBM GB/s ((N+1)*valid bytes / time) and % of MI355X peak",
         "value": round(gbs, 2),
@@ -262,7 +299,7 @@ def main() -> int:
         "config": {
             "workload": name, "op": op, "nranks": w.nranks, "rows": w.rows, "cols": w.cols,
             "ld": w.ld, "valid_rows": w.valid_rows, "valid_cols": w.valid_cols, "root": w.root,
-            "values": w.recipe, "algorithmic_bytes_per_step": algo_bytes,
+            "values": w.recipe, "mode": mode, "algorithmic_bytes_per_step": algo_bytes,
         },
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "elements_per_s": round(elems_s, 1),
@@ -273,11 +310,11 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "treduce_kernel",
+            "kernel": "accumulate_kernel" if mode == "accumulate_add" else "treduce_kernel",
             "kernel_source_hash": kernel_source_hash(),
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and mode == "treduce":
         gpu_bits = dst_t.cpu().numpy().view(W.STORAGE[w.dtype])
         line["cpu_baseline"] = cpu_baseline(w, op, srcs, gpu_bits)
     print(json.dumps(line), flush=True)
