@@ -35,6 +35,7 @@ PTORED_FORCE_ROWS = 0x2
 PTORED_FORCE_RUNTIME_N = 0x4
 PTORED_NO_XCD_REMAP = 0x8
 PTORED_ROW_TILES = 0x10
+PTORED_LDS_PINGPONG = 0x20
 
 PATHS = {0: "none", 1: "copy", 2: "vec_fixed", 3: "vec_runtime", 4: "elementwise"}
 

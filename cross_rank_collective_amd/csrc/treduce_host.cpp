@@ -129,6 +129,10 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         } else if (nranks == 1) {
             p.family = kFamCopy;
             p.unroll = unroll_for(1);
+        } else if ((flags & PTORED_LDS_PINGPONG) != 0 && mode == kModeReduce) {
+            p.family = kFamVecRuntime;  // runtime rank count through LDS stages
+            p.lds_stages = true;
+            p.unroll = 1;
         } else if (nranks <= 16 && (flags & PTORED_FORCE_RUNTIME_N) == 0) {
             p.family = kFamVecFixed;
             p.unroll = unroll_for(nranks);
@@ -151,7 +155,8 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         // fetched twice), yet on MI355X the flattened walk measured faster
         // on ragged rows, so it stays the default.
         p.rows_mode = kWalkFlat;
-        if (p.family != kFamElem && mode == kModeReduce && (flags & PTORED_ROW_TILES) != 0) {
+        if (p.family != kFamElem && mode == kModeReduce && !p.lds_stages &&
+            (flags & PTORED_ROW_TILES) != 0) {
             const int64_t full = valid_cols / vec;
             const int64_t per_tile = (int64_t)kBlock * p.unroll;
             const int64_t tiles = (full + per_tile - 1) / per_tile;

@@ -532,6 +532,93 @@ __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
     }
 }
 
+// ------------------------------------------------------------------------
+// LDS ping-pong variant (the pages' ping/pong recv tiles, [TREDUCE] §2.2 and
+// §4.4): every wave streams the sources through a ring of S 1-KiB LDS stages
+// with gfx950's direct buffer-to-LDS loads, folding stage k while the loads
+// of ranks k+1 .. k+S-1 are in flight.  Each lane reads back exactly the 16
+// bytes it loaded (the load writes lane l's data at stage + 16 l), so the
+// stages are private to the wave and need no barrier.  The compiler does not
+// order an LDS read after the load that fills it, so the waits are explicit:
+// s_waitcnt vmcnt(n) before a stage is read (n = loads issued after it); the
+// read itself waits lgkmcnt(0) before the stage is refilled.
+// ------------------------------------------------------------------------
+
+// s_waitcnt immediates (gfx9 encoding): wait for vmcnt <= n only / lgkmcnt == 0 only.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// wait until at most n (0 <= n < S) vector loads of this wave are outstanding
+template <int S>
+__device__ __forceinline__ void wait_vmcnt_upto(uint32_t n) {
+    if constexpr (S > 1) {
+        if (n >= (uint32_t)(S - 1)) {
+            wait_vmcnt<S - 1>();
+            return;
+        }
+        wait_vmcnt_upto<S - 1>(n);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Read 16 bytes of LDS and wait for them.  Written as one asm block so the
+// compiler, which cannot tell which in-flight LDS load this read depends on,
+// does not add a wait for all of them; the caller's vmcnt wait orders it.
+__device__ __forceinline__ u32x4 lds_read16(const uint32_t* p) {
+    u32x4 v;
+    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+template <int S>
+struct LdsStages {
+    // [wave][stage][64 lanes x 16 bytes]
+    uint32_t words[kBlock / 64][S][256];
+};
+
+template <int DT, int OP, int S, int WALK>
+__device__ __forceinline__ void main_tile_lds(const KArgs& a, uint32_t t, LdsStages<S>& st) {
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t off = slot_offset<WALK>(a, t * (uint32_t)kBlock + wave * 64u + lane);
+    const uint32_t n = a.nranks;
+    // prologue: the first min(S, N) ranks
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+        if ((uint32_t)k < n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a.src[k], a.extent),
+                                                     (lds_ptr_t)&st.words[wave][k][0], 16, off,
+                                                     0, 0, kLoadPolicy);
+    }
+    Acc<DT, OP> acc[4];
+    for (uint32_t k = 0; k < n; ++k) {
+        const uint32_t after = min((uint32_t)(S - 1), n - 1 - k);  // loads issued after k
+        wait_vmcnt_upto<S>(after);
+        const uint32_t slot = k % (uint32_t)S;
+        const u32x4 x = lds_read16(&st.words[wave][slot][lane * 4]);
+        if (k + S < n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a.src[k + S], a.extent),
+                                                     (lds_ptr_t)&st.words[wave][slot][0], 16,
+                                                     off, 0, 0, kLoadPolicy);
+        if (k == 0) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) acc[w].init(x[w]);
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) acc[w].add(x[w]);
+        }
+    }
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) out[w] = acc[w].get();
+    store16(make_rsrc(a.dst, a.extent), off, out);
+}
+
 // One tail tile of the element-wise path: kElemUnroll elements per thread,
 // element by element.
 template <int DT, int OP, int ES, int NR, int WALK, bool ALL>
@@ -633,6 +720,22 @@ __global__ __launch_bounds__(kBlock) void treduce_kernel(const KArgs a) {
             }
         } else {
             element_tile<DT, OP, ES, NR, WALK, ALL>(a, t);
+        }
+    }
+}
+
+// The LDS ping-pong kernel: main tiles through LDS stages (one slot per
+// thread), row remainders as in treduce_kernel.  Runtime rank count.
+template <int DT, int OP, int ES, int WALK, int S>
+__global__ __launch_bounds__(kBlock) void treduce_lds_kernel(const KArgs a) {
+    __shared__ LdsStages<S> stages;
+    const uint32_t grid = gridDim.x;
+    for (uint32_t t = logical_block(blockIdx.x, grid, a.xcd_remap != 0u); t < a.total_tiles;
+         t += grid) {
+        if (t < a.main_tiles) {
+            main_tile_lds<DT, OP, S, WALK>(a, t, stages);
+        } else {
+            row_tail_tile<DT, OP, ES, 0, false>(a, t - a.main_tiles);
         }
     }
 }

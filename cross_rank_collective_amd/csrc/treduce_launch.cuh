@@ -75,6 +75,17 @@ static int dispatch_op(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
         default: return -1;
         }
     }
+    if (p.lds_stages) {  // LDS ping-pong variant: contiguous or flattened walks
+        switch (p.rows_mode) {
+        case kWalkContig:
+            launch<treduce_lds_kernel<DT, OP, ES, kWalkContig, kLdsStages>>(p, a, cu, s);
+            return 0;
+        case kWalkFlat:
+            launch<treduce_lds_kernel<DT, OP, ES, kWalkFlat, kLdsStages>>(p, a, cu, s);
+            return 0;
+        default: return -1;
+        }
+    }
     switch (p.rows_mode) {
     case kWalkContig: return dispatch_n<DT, OP, ES, kWalkContig, false>(p, a, cu, s);
     case kWalkRowTiles: return dispatch_n<DT, OP, ES, kWalkRowTiles, false>(p, a, cu, s);

@@ -73,6 +73,7 @@ struct Plan {
     bool xcd_remap;
     bool store_all;     // in-place allreduce: the result goes back into every source
     bool accumulate;    // push-with-add: dst += every source, by atomics
+    bool lds_stages;    // main tiles staged through LDS (ping-pong variant)
     int blocks_per_cu;  // 0: one tile per block; > 0: persistent grid; < 0: at occupancy
     // geometry of the whole call
     int64_t valid_rows;
@@ -95,6 +96,7 @@ constexpr int unroll_for(int nranks) {
     return nranks <= 2 ? 2 : 1;
 }
 constexpr int kElemUnroll = 4;     // elements per thread, element-wise path
+constexpr int kLdsStages = 4;      // LDS stages per wave in the ping-pong variant
 constexpr int kRuntimeUnroll = 2;  // slots per thread, runtime rank count
 
 // Launch one kernel of the plan's family on `a`, on a persistent grid sized

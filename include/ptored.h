@@ -118,6 +118,9 @@ int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int
 #define PTORED_ROW_TILES 0x10u        /* 2-D region: tiles of one row's column chunk (the pages'
                                          2-D sliding chunk walk) instead of slots numbered
                                          straight through the rows */
+#define PTORED_LDS_PINGPONG 0x20u     /* stage the sources through a ring of LDS buffers with
+                                         direct buffer-to-LDS loads (the pages' ping/pong
+                                         tiles) instead of registers; N >= 2, 16-byte data */
 
 /* Launch choices of ptored_treduce_ex. */
 typedef struct ptored_tuning {

@@ -123,6 +123,10 @@ def test_plan_paths():
     assert B.PATHS[_plan(tuning=t).path] == "elementwise"
     t = B.tuning(flags=B.PTORED_FORCE_RUNTIME_N)
     assert B.PATHS[_plan(tuning=t).path] == "vec_runtime"
+    t = B.tuning(flags=B.PTORED_LDS_PINGPONG)
+    info = _plan(n=5, srcs=A[:5], tuning=t)
+    assert (B.PATHS[info.path], info.slots_per_thread) == ("vec_runtime", 1)
+    assert B.PATHS[_plan(n=1, tuning=t).path] == "copy"  # one rank: nothing to stage
 
 
 def test_plan_walk_and_slots():

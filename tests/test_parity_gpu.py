@@ -84,6 +84,7 @@ VARIANTS = [
     ("rows", B.PTORED_FORCE_ROWS, 0),
     ("row_tiles", B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES, 0),
     ("runtime_n", B.PTORED_FORCE_RUNTIME_N, 0),
+    ("lds_pingpong", B.PTORED_LDS_PINGPONG, 0),
     ("persistent_noremap", B.PTORED_NO_XCD_REMAP, 2),
     ("one_block_per_cu", 0, 1),
     ("persistent_occupancy", 0, -1),
@@ -140,6 +141,10 @@ def test_medium_cases_span_many_tiles(dtype):
                                          (9, OPS[(case + 1) % 4], "rows", B.PTORED_FORCE_ROWS, 0),
                                          (6, OPS[(case + 1) % 4], "row_tiles",
                                           B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES, 0),
+                                         (11, OPS[(case + 2) % 4], "lds_pingpong",
+                                          B.PTORED_LDS_PINGPONG, 0),
+                                         (2, OPS[(case + 3) % 4], "lds_pingpong_n2",
+                                          B.PTORED_LDS_PINGPONG, 1),
                                          (16, OPS[(case + 2) % 4], "auto", 0, 0),
                                          (20, OPS[(case + 3) % 4], "runtime_n", 0, 0),
                                          (3, OPS[case % 4], "elementwise",
@@ -283,7 +288,8 @@ def test_workload_full_size(name):
     srcs = _workload_srcs(w)
     rng = np.random.default_rng(7)
     full_compare = w.dtype == "i32" or w.buffer_elems <= 1 << 21
-    variants = [("auto", 0), ("row_tiles", B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES)]
+    variants = [("auto", 0), ("row_tiles", B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES),
+                ("lds_pingpong", B.PTORED_LDS_PINGPONG)]
     if w.valid_cols == w.ld:
         variants.append(("rows", B.PTORED_FORCE_ROWS))  # the flattened 2-D walk, same data
     es = w.esize
