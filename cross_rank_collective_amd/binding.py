@@ -36,6 +36,7 @@ PTORED_FORCE_RUNTIME_N = 0x4
 PTORED_NO_XCD_REMAP = 0x8
 PTORED_ROW_TILES = 0x10
 PTORED_LDS_PINGPONG = 0x20
+PTORED_SEGMENT_LAUNCHES = 0x40
 
 PATHS = {0: "none", 1: "copy", 2: "vec_fixed", 3: "vec_runtime", 4: "elementwise"}
 

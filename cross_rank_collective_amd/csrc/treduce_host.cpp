@@ -397,6 +397,70 @@ void ring_bounds(int64_t count, int nranks, int dtype, int64_t* bounds) {
     bounds[nranks] = count;
 }
 
+int launch_ring(const Plan& p, const RingArgs& a, int cu, hipStream_t s) {
+    switch (p.dtype) {
+    case PTORED_F32: return launch_ring_f32(p, a, cu, s);
+    case PTORED_BF16: return launch_ring_bf16(p, a, cu, s);
+    case PTORED_F16: return launch_ring_f16(p, a, cu, s);
+    default: return launch_ring_i32(p, a, cu, s);
+    }
+}
+
+// The ring reduce-scatter in one launch per window of max_launch_bytes (one
+// launch in all for streams up to 2 GiB).  Every stream is 16-byte aligned,
+// so window offsets that are multiples of 16 keep whole slots whole.
+// `bounds` are the segment boundaries in elements.
+int run_ring(const Plan& p, const void* const* srcs, void* const* dsts, const int64_t* bounds,
+             int64_t count, hipStream_t stream) {
+    int cu = 0;
+    int st = cu_count_of_current_device(cu);
+    if (st != PTORED_OK) return st;
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    const int n = p.nranks;
+    const int64_t es = p.esize, total = count * es;
+    RingArgs a{};
+    a.nranks = (uint32_t)n;
+    a.xcd_remap = p.xcd_remap ? 1u : 0u;
+    int rc = 0;
+    for (int64_t w0 = 0; w0 < total && rc == 0; w0 += p.max_launch_bytes) {
+        const int64_t w1 = std::min(total, w0 + p.max_launch_bytes);
+        int s0 = -1, s1 = -1;  // segments that meet [w0, w1)
+        for (int s = 0; s < n; ++s)
+            if (bounds[s] * es < w1 && bounds[s + 1] * es > w0) {
+                if (s0 < 0) s0 = s;
+                s1 = s;
+            }
+        if (s0 < 0) continue;
+        for (int s = 0; s <= n; ++s)
+            a.bounds[s] = (uint32_t)std::clamp<int64_t>(bounds[s] * es - w0, 0, w1 - w0);
+        uint32_t main_max = 0, edge = 0;
+        for (int s = s0; s <= s1; ++s) {
+            const uint32_t lo = a.bounds[s], hi = a.bounds[s + 1];
+            const uint32_t first = (lo + 15u) & ~15u, end = hi & ~15u;
+            const uint32_t nslots = first < end ? (end - first) / 16u : 0u;
+            main_max = std::max(main_max, (nslots + (uint32_t)kBlock - 1) / (uint32_t)kBlock);
+            const uint32_t head_end = std::min(hi, first);
+            const uint32_t tail_lo = first <= end ? end : hi;
+            if (head_end > lo || hi > tail_lo) edge = 1;
+        }
+        if (main_max + edge == 0) continue;
+        for (int r = 0; r < n; ++r) {
+            a.src[r] = a.src[r + n] = static_cast<const char*>(srcs[r]) + w0;
+            a.dst[r] = static_cast<char*>(dsts[r]) + w0;
+        }
+        a.extent = (uint32_t)(w1 - w0);
+        a.seg0 = (uint32_t)s0;
+        a.nseg = (uint32_t)(s1 - s0 + 1);
+        a.edge = edge;
+        a.tiles_per_seg = main_max + edge;
+        a.div_seg = fast_div_for(a.tiles_per_seg);
+        rc = launch_ring(p, a, cu, stream);
+    }
+    if (rc != 0) return PTORED_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return PTORED_ERR_HIP;
+    return PTORED_OK;
+}
+
 }  // namespace
 }  // namespace ptored
 
@@ -501,6 +565,16 @@ extern "C" int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, v
     }
     int64_t bounds[PTORED_MAX_RANKS + 1];
     ring_bounds(count, nranks, dtype, bounds);
+    const uint32_t flags = tuning ? tuning->flags : 0u;
+    if (nranks >= 2 && count > 0 && (flags & PTORED_SEGMENT_LAUNCHES) == 0) {
+        // One launch over every segment when all 2N streams take 16-byte slots.
+        Plan p;
+        st = make_plan(ptrs, 2 * nranks, nranks, 1, count, count, dtype, op, tuning, kModeReduce,
+                       p);
+        if (st != PTORED_OK) return st;
+        if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages)
+            return run_ring(p, srcs, dsts, bounds, count, stream);
+    }
     const int es = esize_of(dtype);
     for (int s = 0; s < nranks; ++s) {
         const int64_t lo = bounds[s], len = bounds[s + 1] - bounds[s];

@@ -443,6 +443,70 @@ __device__ __forceinline__ uint32_t fold_word(const u32x4 (&x)[NR][U], int u, in
     return acc.get();
 }
 
+// Load U slots at byte offsets off[] from NR sources (NR == 0: n at run
+// time), source k through src(k), and fold them in order k = 0, 1, ...
+// into out[].  Every load of a slot is issued before its fold starts.
+template <int DT, int OP, int NR, int U, class SrcFn>
+__device__ __forceinline__ void fold_slots(SrcFn src, uint32_t n, const uint32_t (&off)[U],
+                                           u32x4 (&out)[U]) {
+    if constexpr (NR > 0) {
+        u32x4 x[NR][U];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const rsrc_t r = src((uint32_t)k);
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[k][u] = load16(r, off[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[u][w] = fold_word<DT, OP, NR, U>(x, u, w);
+    } else {
+        // Runtime rank count: groups of four sources in flight, then the
+        // remainder one at a time, always in order.
+        Acc<DT, OP> acc[U][4];
+        {
+            const rsrc_t r = src(0u);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const u32x4 x0 = load16(r, off[u]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) acc[u][w].init(x0[w]);
+            }
+        }
+        uint32_t k = 1;
+        for (; k + 4 <= n; k += 4) {
+            u32x4 x[4][U];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const rsrc_t r = src(k + (uint32_t)g);
+#pragma unroll
+                for (int u = 0; u < U; ++u) x[g][u] = load16(r, off[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    acc[u][w].add2(x[0][u][w], x[1][u][w]);
+                    acc[u][w].add2(x[2][u][w], x[3][u][w]);
+                }
+        }
+        for (; k < n; ++k) {
+            const rsrc_t r = src(k);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const u32x4 x = load16(r, off[u]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) acc[u][w].add(x[w]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[u][w] = acc[u][w].get();
+    }
+}
+
 // One main tile: U full 16-byte slots per thread, NR sources.  Row tiles:
 // tile t is column chunk c of row r (t = r * tiles_per_row + c, split on
 // the scalar unit), so every wave's 1 KiB run starts 1 KiB into a row and
@@ -468,68 +532,11 @@ __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
         for (int u = 0; u < U; ++u) off[u] = slot_offset<WALK>(a, base + (uint32_t)(u * 64));
     }
     const rsrc_t rd = make_rsrc(a.dst, a.extent);
-    if constexpr (NR > 0) {
-        u32x4 x[NR][U];
+    u32x4 out[U];
+    fold_slots<DT, OP, NR, U>([&](uint32_t k) { return make_rsrc(a.src[k], a.extent); },
+                              a.nranks, off, out);
 #pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            const rsrc_t r = make_rsrc(a.src[k], a.extent);
-#pragma unroll
-            for (int u = 0; u < U; ++u) x[k][u] = load16(r, off[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            u32x4 out;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) out[w] = fold_word<DT, OP, NR, U>(x, u, w);
-            store_result<ALL>(a, rd, off[u], out);
-        }
-    } else {
-        // Runtime rank count: groups of four sources in flight, then the
-        // remainder one at a time, always in rank order.
-        Acc<DT, OP> acc[U][4];
-        {
-            const rsrc_t r = make_rsrc(a.src[0], a.extent);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const u32x4 x0 = load16(r, off[u]);
-#pragma unroll
-                for (int w = 0; w < 4; ++w) acc[u][w].init(x0[w]);
-            }
-        }
-        uint32_t k = 1;
-        for (; k + 4 <= a.nranks; k += 4) {
-            u32x4 x[4][U];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const rsrc_t r = make_rsrc(a.src[k + g], a.extent);
-#pragma unroll
-                for (int u = 0; u < U; ++u) x[g][u] = load16(r, off[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    acc[u][w].add2(x[0][u][w], x[1][u][w]);
-                    acc[u][w].add2(x[2][u][w], x[3][u][w]);
-                }
-        }
-        for (; k < a.nranks; ++k) {
-            const rsrc_t r = make_rsrc(a.src[k], a.extent);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const u32x4 x = load16(r, off[u]);
-#pragma unroll
-                for (int w = 0; w < 4; ++w) acc[u][w].add(x[w]);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            u32x4 out;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) out[w] = acc[u][w].get();
-            store_result<ALL>(a, rd, off[u], out);
-        }
-    }
+    for (int u = 0; u < U; ++u) store_result<ALL>(a, rd, off[u], out[u]);
 }
 
 // ------------------------------------------------------------------------

@@ -8,18 +8,20 @@
 #pragma once
 
 #include "accumulate_kernels.cuh"
+#include "ring_kernels.cuh"
 #include "treduce_kernels.cuh"
 
 namespace ptored {
 
-// Launch KERNEL over a.total_tiles tiles.  Default (blocks_per_cu == 0):
-// one block per tile, so the dispatcher hands tiles to whichever CU frees
-// up first -- on MI355X this beat every persistent grid size measured.
+// Launch KERNEL over `tiles` tiles.  Default (blocks_per_cu == 0): one
+// block per tile, so the dispatcher hands tiles to whichever CU frees up
+// first -- on MI355X this beat every persistent grid size measured.
 // blocks_per_cu > 0: a persistent grid of that many blocks per CU;
 // blocks_per_cu < 0: a persistent grid at the kernel's occupancy.
-template <auto KERNEL>
-static void launch(const Plan& p, const KArgs& a, int cu_count, hipStream_t s) {
-    uint64_t grid = a.total_tiles;
+template <auto KERNEL, class ARGS>
+static void launch_grid(const Plan& p, const ARGS& a, uint64_t tiles, int cu_count,
+                        hipStream_t s) {
+    uint64_t grid = tiles;
     if (p.blocks_per_cu != 0) {
         int per_cu = p.blocks_per_cu;
         if (per_cu < 0) {
@@ -38,6 +40,11 @@ static void launch(const Plan& p, const KArgs& a, int cu_count, hipStream_t s) {
     }
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(KERNEL, dim3((uint32_t)grid), dim3(kBlock), 0, s, a);
+}
+
+template <auto KERNEL>
+static void launch(const Plan& p, const KArgs& a, int cu_count, hipStream_t s) {
+    launch_grid<KERNEL>(p, a, a.total_tiles, cu_count, s);
 }
 
 template <int DT, int OP, int ES, int WALK, bool ALL>
@@ -134,6 +141,37 @@ static int dispatch_copy(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
         break;
     }
     return 0;
+}
+
+// The single-launch ring reduce-scatter: N unrolled for 2 <= N <= 16.
+template <int DT, int OP, int ES>
+static int dispatch_ring_n(const Plan& p, const RingArgs& a, int cu, hipStream_t s) {
+    const uint64_t tiles = (uint64_t)a.nseg * a.tiles_per_seg;
+    switch (p.family == kFamVecFixed ? p.nranks : 0) {
+#define PTORED_CASE(n)                                                  \
+    case n:                                                             \
+        launch_grid<ring_kernel<DT, OP, ES, n>>(p, a, tiles, cu, s);    \
+        return 0;
+        PTORED_CASE(2) PTORED_CASE(3) PTORED_CASE(4) PTORED_CASE(5) PTORED_CASE(6)
+        PTORED_CASE(7) PTORED_CASE(8) PTORED_CASE(9) PTORED_CASE(10) PTORED_CASE(11)
+        PTORED_CASE(12) PTORED_CASE(13) PTORED_CASE(14) PTORED_CASE(15) PTORED_CASE(16)
+#undef PTORED_CASE
+    case 0:
+        launch_grid<ring_kernel<DT, OP, ES, 0>>(p, a, tiles, cu, s);
+        return 0;
+    default: return -1;
+    }
+}
+
+template <int DT, int ES>
+static int dispatch_ring(const Plan& p, const RingArgs& a, int cu, hipStream_t s) {
+    switch (p.op) {
+    case PTORED_SUM: return dispatch_ring_n<DT, PTORED_SUM, ES>(p, a, cu, s);
+    case PTORED_MAX: return dispatch_ring_n<DT, PTORED_MAX, ES>(p, a, cu, s);
+    case PTORED_MIN: return dispatch_ring_n<DT, PTORED_MIN, ES>(p, a, cu, s);
+    case PTORED_PROD: return dispatch_ring_n<DT, PTORED_PROD, ES>(p, a, cu, s);
+    default: return -1;
+    }
 }
 
 template <int DT, int ES>

@@ -44,6 +44,26 @@ struct KArgs {
     uint32_t xcd_remap;      // 1: per-XCD contiguous tile bands (persistent grids)
 };
 
+// Kernel arguments of one launch of the single-launch ring reduce-scatter
+// (~1.8 KB of kernarg): a window of the N streams, cut into the ring's
+// segments.  Segment s is folded in the order of ranks s+1, s+2, ..., s
+// (mod N) and written to dst[s].  The source table holds the N streams
+// twice over, so that order is src[s + 1], ..., src[s + N] -- consecutive
+// entries from a per-workgroup base, fetched by wide scalar loads.
+struct RingArgs {
+    const void* src[2 * PTORED_MAX_RANKS]; // src[r] = src[r + N] = rank r's stream
+    void* dst[PTORED_MAX_RANKS];         // dst of segment s at the window start
+    uint32_t bounds[PTORED_MAX_RANKS + 1]; // byte offset of segment s in the window (clipped)
+    uint32_t nranks;
+    uint32_t extent;         // bytes of the window
+    uint32_t seg0;           // first segment of the launch
+    uint32_t nseg;           // segments of the launch
+    uint32_t tiles_per_seg;  // main tiles of the largest segment, + 1 with ragged ends
+    uint32_t edge;           // 1: the last tile of every segment folds its ragged ends
+    FastDiv div_seg;         // division by tiles_per_seg
+    uint32_t xcd_remap;      // as KArgs::xcd_remap
+};
+
 // Walks of the valid rectangle (values of Plan::walk and ptored_plan_info.rows_mode).
 enum Walk : int {
     kWalkContig = 0,    // one contiguous span
@@ -106,5 +126,10 @@ int launch_f32(const Plan& p, const KArgs& a, int cu_count, hipStream_t stream);
 int launch_bf16(const Plan& p, const KArgs& a, int cu_count, hipStream_t stream);
 int launch_f16(const Plan& p, const KArgs& a, int cu_count, hipStream_t stream);
 int launch_i32(const Plan& p, const KArgs& a, int cu_count, hipStream_t stream);
+// The single-launch ring reduce-scatter (vector families only).
+int launch_ring_f32(const Plan& p, const RingArgs& a, int cu_count, hipStream_t stream);
+int launch_ring_bf16(const Plan& p, const RingArgs& a, int cu_count, hipStream_t stream);
+int launch_ring_f16(const Plan& p, const RingArgs& a, int cu_count, hipStream_t stream);
+int launch_ring_i32(const Plan& p, const RingArgs& a, int cu_count, hipStream_t stream);
 
 }  // namespace ptored

@@ -121,6 +121,8 @@ int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int
 #define PTORED_LDS_PINGPONG 0x20u     /* stage the sources through a ring of LDS buffers with
                                          direct buffer-to-LDS loads (the pages' ping/pong
                                          tiles) instead of registers; N >= 2, 16-byte data */
+#define PTORED_SEGMENT_LAUNCHES 0x40u /* reduce-scatter: one launch per ring segment instead of
+                                         one launch over every segment */
 
 /* Launch choices of ptored_treduce_ex. */
 typedef struct ptored_tuning {
@@ -200,7 +202,12 @@ int ptored_ring_bounds(int64_t count, int nranks, int dtype, int64_t* bounds);
  *             elements.  dsts[s] may be srcs[s] (in place into the owner's
  *             window), any other source or another dst; partial overlaps are
  *             rejected.
- * Errors as ptored_treduce_ex.  One launch per non-empty segment.
+ * Errors as ptored_treduce_ex.  When every source and dst is 16-byte
+ * aligned, one launch covers every segment (a window of at most
+ * max_launch_bytes per launch): each workgroup takes one segment's tile and
+ * folds it in that segment's ring order, and one more tile per segment
+ * folds its elements outside whole 16-byte slots.  Otherwise, or with
+ * PTORED_SEGMENT_LAUNCHES, one launch per non-empty segment.
  */
 int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, void* const* dsts,
                                int64_t count, int dtype, int op, const ptored_tuning* tuning,

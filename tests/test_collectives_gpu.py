@@ -114,26 +114,45 @@ def test_allreduce_full_size_workload():
 
 # ------------------------------------------------------ ring reduce-scatter ---
 
+# Launch variants of the reduce-scatter: (label, flags, blocks_per_cu,
+# max_launch_bytes, misaligned dst 0).  The default takes one launch over
+# every segment when all streams are 16-byte aligned; the misaligned case
+# and PTORED_SEGMENT_LAUNCHES take one launch per segment.
+RING_VARIANTS = [
+    ("single", 0, 0, 0, False),
+    ("elementwise", B.PTORED_FORCE_ELEMENTWISE, 0, 0, False),
+    ("runtime_n", B.PTORED_FORCE_RUNTIME_N, 0, 0, False),
+    ("per_segment", B.PTORED_SEGMENT_LAUNCHES, 0, 0, False),
+    ("windows_1008", 0, 0, 1008, False),
+    ("persistent", 0, 1, 0, False),
+    ("misaligned", 0, 0, 0, True),
+    ("windows_4096", B.PTORED_FORCE_RUNTIME_N, 0, 4096, False),
+]
+
+
 @pytest.mark.parametrize("dtype", DT)
 def test_reduce_scatter_ring_random(dtype):
     rng = np.random.default_rng({"f32": 41, "bf16": 42, "f16": 43, "i32": 44}[dtype])
-    for case in range(24):
-        n = int(rng.choice([1, 2, 3, 4, 7, 8, 16, 20]))
-        count = int(rng.choice([0, 1, 5, 20, 63, 1000, 4099, 70001]))
+    for case in range(40):
+        n = int(rng.choice([1, 2, 3, 4, 7, 8, 16, 20, 64]))
+        count = int(rng.choice([0, 1, 5, 20, 63, 100, 1000, 4099, 70001]))
         op = OPS[case % 4]
-        flags = [0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_FORCE_RUNTIME_N, 0][case % 4]
-        in_place = case % 3 == 0
+        label, flags, bpc, mlb, misaligned = RING_VARIANTS[case % len(RING_VARIANTS)]
+        in_place = case % 3 == 0 and not misaligned
         srcs = [_rand_elems(dtype, rng, max(count, 1), wild=0.05) for _ in range(n)]
         sb = _upload(srcs, [0] * n)
         if in_place:
             db = sb
             d0 = [s.copy() for s in srcs]
         else:
-            db = [DevBuf(max(count, 1) * ESIZE[dtype], 0, fill=0xFF) for _ in range(n)]
+            offs = [ESIZE[dtype] if (misaligned and s == 0) else 0 for s in range(n)]
+            db = [DevBuf(max(count, 1) * ESIZE[dtype], o, fill=0xFF) for o in offs]
             d0 = [sentinel(dtype, max(count, 1)) for _ in range(n)]
-        say(f"ring#{case} {dtype} {op} N={n} count={count} in_place={in_place} flags={flags}")
+        say(f"ring#{case} {dtype} {op} N={n} count={count} in_place={in_place} {label}")
         st = B.ptored_reduce_scatter_ring([b.ptr for b in sb], n, [b.ptr for b in db], count,
-                                          B.DTYPES[dtype], B.OPS[op], B.tuning(flags=flags),
+                                          B.DTYPES[dtype], B.OPS[op],
+                                          B.tuning(flags=flags, blocks_per_cu=bpc,
+                                                   max_launch_bytes=mlb),
                                           _stream())
         torch.cuda.synchronize()
         assert st == 0, B.ptored_status_string(st)
@@ -143,6 +162,31 @@ def test_reduce_scatter_ring_random(dtype):
         for s in range(n):
             got = db[s].download(dtype)
             assert compare(dtype, got, want[s]).all(), (case, s)
+            assert db[s].guards_intact()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_reduce_scatter_ring_ragged_segments(dtype):
+    """Segment bounds off the 16-byte grid (f32: floor(i * count / N) with
+    count not a multiple of 4N; bf16: the last segment short or empty), and
+    windows whose edges fall inside segments, on the single-launch path."""
+    rng = np.random.default_rng(47)
+    for count, n, mlb in ((4099, 7, 0), (4099, 7, 528), (37, 5, 0), (17, 16, 0),
+                          (33, 3, 16), (65537, 16, 8192), (250, 64, 0)):
+        srcs = [_rand_elems(dtype, rng, count, wild=0.05) for _ in range(n)]
+        sb = _upload(srcs, [0] * n)
+        db = [DevBuf(count * ESIZE[dtype], 0, fill=0xFF) for _ in range(n)]
+        say(f"ring ragged {dtype} count={count} N={n} mlb={mlb}")
+        st = B.ptored_reduce_scatter_ring([b.ptr for b in sb], n, [b.ptr for b in db], count,
+                                          B.DTYPES[dtype], B.OPS["sum"],
+                                          B.tuning(max_launch_bytes=mlb), _stream())
+        torch.cuda.synchronize()
+        assert st == 0, B.ptored_status_string(st)
+        want = [sentinel(dtype, count) for _ in range(n)]
+        oracle.reduce_scatter_ring([s.copy() for s in srcs], want, count=count, dtype=dtype,
+                                   op="sum")
+        for s in range(n):
+            assert compare(dtype, db[s].download(dtype), want[s]).all(), (count, n, mlb, s)
             assert db[s].guards_intact()
 
 
@@ -174,6 +218,41 @@ def test_reduce_scatter_ring_full_size_bf16():
         outside = np.ones(count, bool)
         outside[bounds[s]:bounds[s + 1]] = False
         assert np.array_equal(got[outside], srcs[s][outside])
+
+
+def test_reduce_scatter_ring_full_size_i32():
+    """n16_i32_4096x4096 reduce-scatter into separate dsts: i32 sums wrap and
+    are exact in any order, so every segment is checked whole against the
+    wrapped sum; sampled windows against the oracle's ring-order fold."""
+    w = W.WORKLOADS["n16_i32_4096x4096"]
+    srcs = W.make_sources(w)
+    count = w.buffer_elems
+    sb = _upload(srcs, [0] * w.nranks)
+    db = [DevBuf(count * 4, 0, fill=0xFF) for _ in range(w.nranks)]
+    say("ring full n16_i32_4096x4096 sum")
+    st = B.ptored_reduce_scatter_ring([b.ptr for b in sb], w.nranks, [b.ptr for b in db], count,
+                                      B.DTYPES["i32"], B.OPS["sum"], None, _stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    bounds = oracle.ring_bounds(count, w.nranks, "i32")
+    total = np.zeros(count, np.int64)
+    for x in srcs:
+        total += x
+    total = total.astype(np.uint32).view(np.int32)  # wrap to 32 bits
+    rng = np.random.default_rng(46)
+    for s in range(w.nranks):
+        got = db[s].download("i32")
+        lo, hi = int(bounds[s]), int(bounds[s + 1])
+        assert np.array_equal(got[lo:hi], total[lo:hi]), s
+        assert np.all(got[:lo].view(np.uint32) == 0xFFFFFFFF)
+        assert np.all(got[hi:].view(np.uint32) == 0xFFFFFFFF)
+        a = int(rng.integers(lo, hi - 1024))
+        sub = [np.ascontiguousarray(x[a:a + 1024]) for x in srcs]
+        ring = [sub[(s + 1 + k) % w.nranks] for k in range(w.nranks)]
+        want = sentinel("i32", 1024)
+        oracle.treduce(ring, want, root=0, dtype="i32", op="sum", rows=1, cols=1024, ld=1024,
+                       valid_rows=1, valid_cols=1024)
+        assert np.array_equal(got[a:a + 1024], want), (s, a)
 
 
 # ------------------------------------------------------------ push-with-add ---
