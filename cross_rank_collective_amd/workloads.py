@@ -135,6 +135,32 @@ def draw(recipe: str, n: int, seed: int) -> np.ndarray:
     raise ValueError(f"unknown recipe {recipe!r}")
 
 
+def draw_device(recipe: str, n: int, seed: int, device: str = "cuda"):
+    """n values of one recipe drawn on the device with torch's generator
+    seeded by `seed` (for buffers too large to draw on the host), as a tensor
+    of raw element bits: int32 for the 4-byte types, int16 for the 2-byte
+    ones.  Same distributions as ``draw``; not the same values."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    if recipe == "uniform_pm1":
+        return (torch.rand(n, generator=g, device=device) * 2.0 - 1.0).view(torch.int32)
+    if recipe == "normal_1e-2":
+        x = torch.randn(n, generator=g, device=device) * 1e-2
+        return x.to(torch.bfloat16).view(torch.int16)
+    if recipe == "int_pm2^20":
+        return torch.randint(-(2 ** 20), 2 ** 20, (n,), generator=g, device=device,
+                             dtype=torch.int32)
+    if recipe == "normal_sat":
+        v = torch.randn(n, generator=g, device=device).to(torch.float16)
+        hit = torch.rand(n, generator=g, device=device) < 0.01
+        neg = torch.rand(n, generator=g, device=device) < 0.5
+        sat = torch.where(neg, -65504.0, 65504.0).to(torch.float16)
+        return torch.where(hit, sat, v).view(torch.int16)
+    raise ValueError(f"unknown recipe {recipe!r}")
+
+
 def make_sources(w: Workload, threads: int = 8) -> List[np.ndarray]:
     """The N rank buffers of a workload, each ``rows x ld`` elements.
 
