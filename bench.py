@@ -33,6 +33,29 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 PROFILES = os.path.join(ROOT, "profiles")
+MODES = ["treduce", "allreduce", "reduce_scatter_ring", "accumulate_add"]
+# The kernel each mode launches (one launch per call at the bench's sizes).
+MODE_KERNEL = {"treduce": "treduce_kernel", "allreduce": "treduce_kernel",
+               "reduce_scatter_ring": "ring_kernel", "accumulate_add": "accumulate_kernel"}
+
+
+def algorithmic_bytes(w, mode: str) -> int:
+    """Bytes a call must move: N reads + 1 write of every valid element
+    (reduce); N reads + N writes (in-place allreduce); N reads + 1 write of
+    every element of the stream (ring reduce-scatter); N reads + one read and
+    one write of dst (push-with-add)."""
+    if mode == "treduce":
+        return w.algorithmic_bytes
+    if mode == "allreduce":
+        return 2 * w.nranks * w.valid_bytes
+    if mode == "reduce_scatter_ring":
+        return (w.nranks + 1) * w.buffer_elems * w.esize
+    return (w.nranks + 2) * w.valid_bytes
+
+
+def traffic_path(workload: str, op: str, mode: str) -> str:
+    suffix = "" if mode == "treduce" else f"_{mode}"
+    return os.path.join(PROFILES, f"traffic_{workload}_{op}{suffix}.txt")
 CSRC = os.path.join(ROOT, "cross_rank_collective_amd", "csrc")
 
 
@@ -47,10 +70,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, op: str):
+def stored_traffic(workload: str, op: str, mode: str = "treduce"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none for this kernel source."""
-    path = os.path.join(PROFILES, f"traffic_{workload}_{op}.txt")
+    path = traffic_path(workload, op, mode)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -66,8 +89,8 @@ def stored_traffic(workload: str, op: str):
         return None
 
 
-def _counter_mean_kib(directory: str, counter: str) -> float:
-    """Mean per-dispatch value of one counter for the reduction kernel, from a
+def _counter_mean_kib(directory: str, counter: str, kernel: str = "treduce_kernel") -> float:
+    """Mean per-dispatch value of one counter for one kernel, from a
     rocprofv3 --pmc run written with -f csv under `directory`."""
     import csv
     import glob
@@ -77,11 +100,11 @@ def _counter_mean_kib(directory: str, counter: str) -> float:
                           recursive=True):
         with open(path) as fh:
             for row in csv.DictReader(fh):
-                if "treduce_kernel" in row.get("Kernel_Name", "") and \
+                if kernel in row.get("Kernel_Name", "") and \
                         row.get("Counter_Name") == counter:
                     vals.append(float(row["Counter_Value"]))
     if not vals:
-        raise RuntimeError(f"no {counter} rows for treduce_kernel under {directory}")
+        raise RuntimeError(f"no {counter} rows for {kernel} under {directory}")
     return sum(vals) / len(vals)
 
 
@@ -90,12 +113,14 @@ def summarize_counters(args) -> int:
     FETCH_SIZE and WRITE_SIZE of the workload and of the 1 GiB copy."""
     from cross_rank_collective_amd import workloads as W
 
-    w = W.find(args.workload)
+    w = W.find(args.workload or W.HEADLINE)
     op = args.op or w.ops[0]
+    kernel = MODE_KERNEL[args.mode]
+    algo = algorithmic_bytes(w, args.mode)
     cal = W.CALIBRATION["n1_i32_16384x16384_copy"]
     fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = args.summarize_counters
-    fetch = _counter_mean_kib(fetch_dir, "FETCH_SIZE")
-    write = _counter_mean_kib(write_dir, "WRITE_SIZE")
+    fetch = _counter_mean_kib(fetch_dir, "FETCH_SIZE", kernel)
+    write = _counter_mean_kib(write_dir, "WRITE_SIZE", kernel)
     cal_fetch = _counter_mean_kib(cal_fetch_dir, "FETCH_SIZE")
     cal_write = _counter_mean_kib(cal_write_dir, "WRITE_SIZE")
     copy_bytes = cal.valid_bytes
@@ -103,7 +128,7 @@ def summarize_counters(args) -> int:
     write_scale = copy_bytes / (cal_write * 1024.0)
     traffic = fetch * 1024.0 * fetch_scale + write * 1024.0 * write_scale
     lines = [
-        f"# HBM traffic per launch of treduce_kernel, workload {w.name}, op {op}",
+        f"# HBM traffic per launch of {kernel}, workload {w.name}, op {op}, mode {args.mode}",
         "# from rocprofv3 counters (KiB per dispatch), scaled by a 1 GiB copy",
         f"# ({cal.name}: {copy_bytes} bytes read and written per dispatch).",
         "# commands (each its own run):",
@@ -118,11 +143,11 @@ def summarize_counters(args) -> int:
         f"fetch_scale = {fetch_scale:.5f}",
         f"write_scale = {write_scale:.5f}",
         f"hbm_bytes_per_launch = {traffic:.0f}",
-        f"algorithmic_bytes_per_launch = {w.algorithmic_bytes}",
-        f"traffic_over_algorithmic = {traffic / w.algorithmic_bytes:.4f}",
+        f"algorithmic_bytes_per_launch = {algo}",
+        f"traffic_over_algorithmic = {traffic / algo:.4f}",
     ]
     text = "\n".join(lines) + "\n"
-    out = args.counters_out or os.path.join(PROFILES, f"traffic_{w.name}_{op}.txt")
+    out = args.counters_out or traffic_path(w.name, op, args.mode)
     with open(out, "w") as fh:
         fh.write(text)
     print(text, end="")
@@ -195,8 +220,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--op", default=None)
-    ap.add_argument("--mode", default="treduce",
-                    choices=["treduce", "allreduce", "reduce_scatter_ring", "accumulate_add"])
+    ap.add_argument("--mode", default="treduce", choices=MODES)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -233,30 +257,31 @@ def main() -> int:
     ptrs = [t.data_ptr() for t in src_t]
     dt, opc = B.DTYPES[w.dtype], B.OPS[op]
     mode = args.mode
+    algo_bytes = algorithmic_bytes(w, mode)
+    launches = 1
     if mode == "treduce":
-        algo_bytes = w.algorithmic_bytes
+        st, info = B.ptored_treduce_plan(ptrs, w.nranks, w.root, dst_t.data_ptr(), w.rows,
+                                         w.cols, w.ld, w.valid_rows, w.valid_cols, dt, opc)
+        if st != 0:
+            raise RuntimeError(B.ptored_status_string(st))
+        launches = int(info.launches)
 
         def call():
             return B.ptored_treduce(ptrs, w.nranks, w.root, dst_t.data_ptr(), w.rows, w.cols,
                                     w.ld, w.valid_rows, w.valid_cols, dt, opc,
                                     stream.cuda_stream)
     elif mode == "allreduce":
-        algo_bytes = 2 * w.nranks * w.valid_bytes
-
         def call():
             return B.ptored_allreduce(ptrs, w.nranks, w.root, w.rows, w.cols, w.ld,
                                       w.valid_rows, w.valid_cols, dt, opc, None,
                                       stream.cuda_stream)
     elif mode == "reduce_scatter_ring":
         count = w.buffer_elems
-        algo_bytes = (w.nranks + 1) * count * w.esize
 
         def call():  # in place: segment s goes back into rank s's buffer
             return B.ptored_reduce_scatter_ring(ptrs, w.nranks, ptrs, count, dt, opc, None,
                                                 stream.cuda_stream)
     else:
-        algo_bytes = (w.nranks + 2) * w.valid_bytes
-
         def call():
             return B.ptored_accumulate_add(ptrs, w.nranks, dst_t.data_ptr(), w.rows, w.cols,
                                            w.ld, w.valid_rows, w.valid_cols, dt, None,
@@ -282,7 +307,7 @@ def main() -> int:
     gbs = algo_bytes / (ms_step * 1e-3) / 1e9
     elems_s = w.valid_rows * w.valid_cols / (ms_step * 1e-3)
 
-    traffic = stored_traffic(name, op) if mode == "treduce" else None
+    traffic = stored_traffic(name, op, mode)
     line = {
         "metric": "effective HBM GB/s ((N+1)*valid bytes / time) and % of MI355X peak",
         "value": round(gbs, 2),
@@ -300,6 +325,7 @@ def main() -> int:
             "workload": name, "op": op, "nranks": w.nranks, "rows": w.rows, "cols": w.cols,
             "ld": w.ld, "valid_rows": w.valid_rows, "valid_cols": w.valid_cols, "root": w.root,
             "values": w.recipe, "mode": mode, "algorithmic_bytes_per_step": algo_bytes,
+            "launches_per_step": launches,
         },
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "elements_per_s": round(elems_s, 1),
@@ -310,7 +336,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "accumulate_kernel" if mode == "accumulate_add" else "treduce_kernel",
+            "kernel": MODE_KERNEL[mode],
             "kernel_source_hash": kernel_source_hash(),
         },
     }
