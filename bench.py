@@ -6,14 +6,21 @@ effective HBM GB/s = (N+1) * valid bytes / time, with the roofline of the
 reduce kernel and the CPU oracle timed on a bounded sample as a baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--op OP]
-                    [--mode treduce|allreduce|reduce_scatter_ring|accumulate_add]
+                    [--mode treduce|allreduce|reduce_scatter_ring|accumulate_add|memcpy]
+                    [--sets S]
 
 The default mode is the reduction itself (dst = fold of the N sources); the
 other modes time the collective variants on the same workload: the in-place
 allreduce (N reads + N writes per valid element), the ring reduce-scatter
 share over the whole buffer as one stream (N reads + 1 write per element)
 and push-with-add by atomics (N source reads + one read and one write of dst
-per element, the least any order of the additions must move).
+per element, the least any order of the additions must move); memcpy times
+the runtime's device-to-device copy of one buffer, as a context ceiling.
+
+When one set of input and output buffers fits in the 256 MB Infinity Cache,
+the steps rotate over enough copies of it (``--sets``, default automatic) to
+touch at least 1 GiB between two uses of a set, so the figure is an HBM one;
+``config.residency`` says which it is.
 """
 
 from __future__ import annotations
@@ -33,10 +40,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 PROFILES = os.path.join(ROOT, "profiles")
-MODES = ["treduce", "allreduce", "reduce_scatter_ring", "accumulate_add"]
+MODES = ["treduce", "allreduce", "reduce_scatter_ring", "accumulate_add", "memcpy"]
+MALL_BYTES = 256 << 20   # MI355X Infinity Cache
+ROTATE_BYTES = 1 << 30   # rotate input sets until the steps touch at least this much
+MAX_SETS = 64
 # The kernel each mode launches (one launch per call at the bench's sizes).
 MODE_KERNEL = {"treduce": "treduce_kernel", "allreduce": "treduce_kernel",
-               "reduce_scatter_ring": "ring_kernel", "accumulate_add": "accumulate_kernel"}
+               "reduce_scatter_ring": "ring_kernel", "accumulate_add": "accumulate_kernel",
+               "memcpy": "copyBuffer"}
 
 
 def algorithmic_bytes(w, mode: str) -> int:
@@ -50,6 +61,8 @@ def algorithmic_bytes(w, mode: str) -> int:
         return 2 * w.nranks * w.valid_bytes
     if mode == "reduce_scatter_ring":
         return (w.nranks + 1) * w.buffer_elems * w.esize
+    if mode == "memcpy":  # context: the runtime's copy of one source buffer into dst
+        return 2 * w.buffer_elems * w.esize
     return (w.nranks + 2) * w.valid_bytes
 
 
@@ -164,35 +177,70 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def host_threads() -> int:
+    """Host cores this process may use, at most 16 (one GPU's share of a box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(w, op, srcs, gpu_dst_bits, target_s: float = 10.0):
-    """Time the oracle (single thread, as written) on the first rows of the
-    same workload, sized to about `target_s` seconds, and check the GPU rows
-    against it bit for bit."""
+    """Time the oracle as written on the first rows of the same workload:
+    on one thread, sized to about `target_s` seconds, and on every host core
+    (row bands, one oracle call per band and thread) for about as long; check
+    the GPU rows against it bit for bit."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     from cross_rank_collective_amd import workloads as W
 
-    def run(rows):
+    def band(rows, r0, r1, dst):
+        # rows [r0, r1) of the first `rows` rows, into dst (ctypes drops the GIL)
+        off = r0 * w.ld
+        size = (r1 - r0 - 1) * w.ld + w.cols
+        sub = [s[off:off + size] for s in srcs]
+        oracle.treduce(sub, dst[off:off + size], root=w.root, dtype=w.dtype, op=op,
+                       rows=r1 - r0, cols=w.cols, ld=w.ld, valid_rows=r1 - r0,
+                       valid_cols=w.valid_cols)
+
+    def run(rows, threads=1, pool=None):
         size = (rows - 1) * w.ld + w.cols
-        sub = [np.ascontiguousarray(s[:size]) for s in srcs]
         dst = W.sentinel_buffer(w.dtype, size)
         t0 = time.perf_counter()
-        oracle.treduce(sub, dst, root=w.root, dtype=w.dtype, op=op, rows=rows, cols=w.cols,
-                       ld=w.ld, valid_rows=rows, valid_cols=w.valid_cols)
+        if threads == 1:
+            band(rows, 0, rows, dst)
+        else:
+            cuts = [rows * k // threads for k in range(threads + 1)]
+            list(pool.map(lambda k: band(rows, cuts[k], cuts[k + 1], dst),
+                          [k for k in range(threads) if cuts[k + 1] > cuts[k]]))
         return time.perf_counter() - t0, dst
+
+    def timed(rows, threads, pool, budget):
+        t = run(rows, threads, pool)[0]
+        repeats = 1
+        if t < budget / 2:
+            repeats = int(min(400, budget // max(t, 1e-6)))
+            total = t
+            for _ in range(repeats - 1):
+                total += run(rows, threads, pool)[0]
+            t = total / repeats
+        return t, repeats
 
     probe_rows = min(w.valid_rows, 8)
     t_probe, _ = run(probe_rows)
     rows = int(min(w.valid_rows, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
-    t, dst = run(rows)
+    t1, dst = run(rows)
     # When the whole workload takes well under the target, repeat it and
     # report the mean, so the baseline is not a single short timing.
-    repeats = 1
-    if rows == w.valid_rows and t < target_s / 2:
-        repeats = int(min(30, target_s // max(t, 1e-6)))
-        total = t
-        for _ in range(repeats - 1):
-            total += run(rows)[0]
-        t = total / repeats
+    repeats1 = 1
+    if rows == w.valid_rows and t1 < target_s / 2:
+        t1, repeats1 = timed(rows, 1, None, target_s)
+    threads = host_threads()
+    with ThreadPoolExecutor(threads) as pool:
+        tn, repeats_n = timed(rows, threads, pool, target_s)
+        _, dst_n = run(rows, threads, pool)
     nbytes = (w.nranks + 1) * rows * w.valid_cols * w.esize
     m = np.zeros((rows, w.ld), dtype=bool)
     m[:, :w.valid_cols] = True
@@ -200,16 +248,19 @@ def cpu_baseline(w, op, srcs, gpu_dst_bits, target_s: float = 10.0):
     gpu = gpu_dst_bits[:dst.size]
     same = np.array_equal(gpu.view(np.uint8).reshape(dst.size, -1)[m],
                           dst.view(np.uint8).reshape(dst.size, -1)[m])
+    bands_same = np.array_equal(dst.view(np.uint8), dst_n.view(np.uint8))
     return {
-        "value": round(nbytes / t / 1e9, 4),
+        "value": round(nbytes / tn / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
         "sample": f"first {rows} of {w.valid_rows} valid rows ({rows * w.valid_cols} elements x "
-                  f"{w.nranks} ranks), mean of {repeats} run(s) of {t:.3f} s on 1 thread of "
-                  f"{cpu_model()}",
-        "seconds": round(t, 3),
-        "gpu_rows_bit_exact": bool(same),
+                  f"{w.nranks} ranks), split in {threads} row bands over {threads} threads, "
+                  f"mean of {repeats_n} run(s) of {tn:.4f} s; one thread: mean of {repeats1} "
+                  f"run(s) of {t1:.3f} s; {cpu_model()}",
+        "value_1_thread": round(nbytes / t1 / 1e9, 4),
+        "seconds": round(tn, 4),
+        "gpu_rows_bit_exact": bool(same and bands_same),
     }
 
 
@@ -222,6 +273,9 @@ def main() -> int:
     ap.add_argument("--op", default=None)
     ap.add_argument("--mode", default="treduce", choices=MODES)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets the steps rotate over (0 = enough to defeat the "
+                         "Infinity Cache when one set fits in it)")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the HBM-traffic summary from four rocprofv3 --pmc runs")
@@ -254,41 +308,54 @@ def main() -> int:
     src_t = [torch.from_numpy(s.view(np.uint8)).to(dev) for s in srcs]
     dst_t = torch.full((w.buffer_elems * w.esize,), 0xFF, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    ptrs = [t.data_ptr() for t in src_t]
     dt, opc = B.DTYPES[w.dtype], B.OPS[op]
     mode = args.mode
     algo_bytes = algorithmic_bytes(w, mode)
+    # Input sets: when one set of buffers fits in the Infinity Cache, the
+    # steps rotate over copies so that every step reads from HBM.
+    set_bytes = (2 if mode == "memcpy" else w.nranks + 1) * w.buffer_elems * w.esize
+    nsets = args.sets
+    if nsets <= 0:
+        nsets = 1 if set_bytes >= MALL_BYTES else min(MAX_SETS, -(-ROTATE_BYTES // set_bytes))
+    sets = [(src_t, dst_t)] + [([t.clone() for t in src_t], dst_t.clone())
+                               for _ in range(nsets - 1)]
+    set_ptrs = [[t.data_ptr() for t in srcs_k] for srcs_k, _ in sets]
+    residency = "hbm" if nsets * set_bytes >= ROTATE_BYTES else "cache-resident"
     launches = 1
     if mode == "treduce":
-        st, info = B.ptored_treduce_plan(ptrs, w.nranks, w.root, dst_t.data_ptr(), w.rows,
-                                         w.cols, w.ld, w.valid_rows, w.valid_cols, dt, opc)
+        st, info = B.ptored_treduce_plan([t.data_ptr() for t in src_t], w.nranks, w.root,
+                                         dst_t.data_ptr(), w.rows, w.cols, w.ld, w.valid_rows,
+                                         w.valid_cols, dt, opc)
         if st != 0:
             raise RuntimeError(B.ptored_status_string(st))
         launches = int(info.launches)
 
-        def call():
-            return B.ptored_treduce(ptrs, w.nranks, w.root, dst_t.data_ptr(), w.rows, w.cols,
+    def call(k):
+        srcs_k, dst_k = sets[k]
+        ptrs = set_ptrs[k]
+        if mode == "treduce":
+            return B.ptored_treduce(ptrs, w.nranks, w.root, dst_k.data_ptr(), w.rows, w.cols,
                                     w.ld, w.valid_rows, w.valid_cols, dt, opc,
                                     stream.cuda_stream)
-    elif mode == "allreduce":
-        def call():
+        if mode == "allreduce":
             return B.ptored_allreduce(ptrs, w.nranks, w.root, w.rows, w.cols, w.ld,
                                       w.valid_rows, w.valid_cols, dt, opc, None,
                                       stream.cuda_stream)
-    elif mode == "reduce_scatter_ring":
-        count = w.buffer_elems
-
-        def call():  # in place: segment s goes back into rank s's buffer
-            return B.ptored_reduce_scatter_ring(ptrs, w.nranks, ptrs, count, dt, opc, None,
-                                                stream.cuda_stream)
-    else:
-        def call():
-            return B.ptored_accumulate_add(ptrs, w.nranks, dst_t.data_ptr(), w.rows, w.cols,
+        if mode == "reduce_scatter_ring":  # in place: segment s back into rank s's buffer
+            return B.ptored_reduce_scatter_ring(ptrs, w.nranks, ptrs, w.buffer_elems, dt, opc,
+                                                None, stream.cuda_stream)
+        if mode == "accumulate_add":
+            return B.ptored_accumulate_add(ptrs, w.nranks, dst_k.data_ptr(), w.rows, w.cols,
                                            w.ld, w.valid_rows, w.valid_cols, dt, None,
                                            stream.cuda_stream)
+        dst_k.copy_(srcs_k[0])  # memcpy: the runtime's device-to-device copy
+        return 0
+
+    nstep = [0]
 
     def step():
-        st = call()
+        st = call(nstep[0] % nsets)
+        nstep[0] += 1
         if st != 0:
             raise RuntimeError(B.ptored_status_string(st))
 
@@ -307,7 +374,7 @@ def main() -> int:
     gbs = algo_bytes / (ms_step * 1e-3) / 1e9
     elems_s = w.valid_rows * w.valid_cols / (ms_step * 1e-3)
 
-    traffic = stored_traffic(name, op, mode)
+    traffic = stored_traffic(name, op, mode) if mode != "memcpy" else None
     line = {
         "metric": "effective HBM GB/s ((N+1)*valid bytes / time) and % of MI355X peak",
         "value": round(gbs, 2),
@@ -325,7 +392,7 @@ def main() -> int:
             "workload": name, "op": op, "nranks": w.nranks, "rows": w.rows, "cols": w.cols,
             "ld": w.ld, "valid_rows": w.valid_rows, "valid_cols": w.valid_cols, "root": w.root,
             "values": w.recipe, "mode": mode, "algorithmic_bytes_per_step": algo_bytes,
-            "launches_per_step": launches,
+            "launches_per_step": launches, "input_sets": nsets, "residency": residency,
         },
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "elements_per_s": round(elems_s, 1),
