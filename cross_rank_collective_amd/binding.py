@@ -37,6 +37,7 @@ PTORED_NO_XCD_REMAP = 0x8
 PTORED_ROW_TILES = 0x10
 PTORED_LDS_PINGPONG = 0x20
 PTORED_SEGMENT_LAUNCHES = 0x40
+PTORED_FULL_OCCUPANCY = 0x80
 
 PATHS = {0: "none", 1: "copy", 2: "vec_fixed", 3: "vec_runtime", 4: "elementwise"}
 
@@ -49,7 +50,8 @@ class ptored_tuning(ctypes.Structure):
 class ptored_plan_info(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("rows_mode", ctypes.c_int32),
                 ("vec_elems", ctypes.c_int32), ("slots_per_thread", ctypes.c_int32),
-                ("slots", ctypes.c_int64), ("launches", ctypes.c_int64)]
+                ("slots", ctypes.c_int64), ("launches", ctypes.c_int64),
+                ("wgs_per_cu", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class PtoredError(RuntimeError):

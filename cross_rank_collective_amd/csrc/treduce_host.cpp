@@ -96,10 +96,12 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
     p.valid_rows = valid_rows;
     p.valid_cols = valid_cols;
     p.ld = ld;
-    p.xcd_remap = (flags & PTORED_NO_XCD_REMAP) == 0;
+    p.blocks_per_cu = tuning ? tuning->blocks_per_cu : 0;
+    // per-XCD bands only for persistent grids: with one tile per block the
+    // dispatcher's round-robin over the XCDs keeps the live tiles contiguous
+    p.xcd_remap = (flags & PTORED_NO_XCD_REMAP) == 0 && p.blocks_per_cu != 0;
     p.store_all = mode == kModeAllreduce;
     p.accumulate = mode == kModeAccumulate;
-    p.blocks_per_cu = tuning ? tuning->blocks_per_cu : 0;
     int64_t mlb = (tuning && tuning->max_launch_bytes > 0) ? tuning->max_launch_bytes
                                                            : kDefaultLaunchBytes;
     mlb = std::min<int64_t>(mlb, kDefaultLaunchBytes);
@@ -144,6 +146,16 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         p.family = kFamElem;
         p.vec_elems = 1;
         p.unroll = kElemUnroll;
+    }
+    // Resident workgroups per CU for one-tile-per-block launches of the
+    // 16-byte kernels (not push-with-add, which is bound by its atomics).
+    if (p.family != kFamElem && mode != kModeAccumulate && p.blocks_per_cu == 0 &&
+        (flags & PTORED_FULL_OCCUPANCY) == 0) {
+        const uint64_t slot_bytes = (uint64_t)kBlock * 16u * (uint64_t)p.unroll;
+        const uint64_t streams = p.family == kFamCopy ? 2u
+                                 : mode == kModeAllreduce ? 2u * (uint64_t)nranks
+                                                          : (uint64_t)nranks + 1u;
+        p.wgs_per_cu = wgs_per_cu_for(streams * slot_bytes);
     }
     const int64_t vec = p.vec_elems;
     if (p.rows_mode) {
@@ -291,25 +303,64 @@ int launch_rows(const Plan& p, KArgs a, const char* const* ordered, char* dst, i
     return launch_one(p, a, cu, s);
 }
 
-std::atomic<int> g_cu_cache[256];
+// Per-device facts the launches need, read once per device.
+struct DeviceFacts {
+    int cu;            // compute units
+    int lds_per_cu;    // LDS bytes per CU
+    int lds_per_block; // LDS bytes one workgroup may hold
+};
+std::atomic<int> g_dev_cu[256], g_dev_lds_cu[256], g_dev_lds_block[256];
 
-int cu_count_of_current_device(int& cu) {
+int facts_of_current_device(DeviceFacts& f) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return PTORED_ERR_HIP;
-    if (dev >= 0 && dev < 256) {
-        const int cached = g_cu_cache[dev].load(std::memory_order_relaxed);
-        if (cached > 0) {
-            cu = cached;
-            return PTORED_OK;
-        }
+    const bool cacheable = dev >= 0 && dev < 256;
+    if (cacheable && g_dev_cu[dev].load(std::memory_order_acquire) > 0) {
+        f.lds_per_cu = g_dev_lds_cu[dev].load(std::memory_order_relaxed);
+        f.lds_per_block = g_dev_lds_block[dev].load(std::memory_order_relaxed);
+        f.cu = g_dev_cu[dev].load(std::memory_order_relaxed);
+        return PTORED_OK;
     }
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n < 1)
+    int cu = 0, lds_cu = 0, lds_block = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu < 1)
         return PTORED_ERR_HIP;
-    if (dev >= 0 && dev < 256) g_cu_cache[dev].store(n, std::memory_order_relaxed);
-    cu = n;
+    if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess) {
+        lds_cu = 0;  // no occupancy limit without these
+        lds_block = 0;
+    }
+    if (cacheable) {
+        g_dev_lds_cu[dev].store(lds_cu, std::memory_order_relaxed);
+        g_dev_lds_block[dev].store(lds_block, std::memory_order_relaxed);
+        g_dev_cu[dev].store(cu, std::memory_order_release);
+    }
+    f.cu = cu;
+    f.lds_per_cu = lds_cu;
+    f.lds_per_block = lds_block;
     return PTORED_OK;
+}
+
+// The LDS reservation that lets exactly `wgs` workgroups share one CU:
+// more than lds_per_cu / (wgs + 1), at most lds_per_cu / wgs, on a 2 KiB
+// grid (coarser than the hardware's allocation unit), and within one
+// workgroup's limit; 0 when no such size exists.
+uint32_t cap_lds_bytes(const DeviceFacts& f, int wgs) {
+    if (wgs < 1 || f.lds_per_cu <= 0) return 0;
+    const int64_t grain = 2048;
+    const int64_t lds = (int64_t)f.lds_per_cu / wgs / grain * grain;
+    if (lds * (wgs + 1) <= (int64_t)f.lds_per_cu || lds > (int64_t)f.lds_per_block) return 0;
+    return (uint32_t)lds;
+}
+
+// The plan with the occupancy limit resolved for this device.
+Plan with_device(const Plan& p, const DeviceFacts& f) {
+    Plan q = p;
+    q.cap_lds = cap_lds_bytes(f, p.wgs_per_cu);
+    q.cap_min_tiles = (uint64_t)kCapMinRounds * (uint64_t)f.cu * (uint64_t)(p.wgs_per_cu > 0 ? p.wgs_per_cu : 0);
+    return q;
 }
 
 // Fold order of [TREDUCE] §4.3: the root's buffer first, then every other
@@ -323,11 +374,13 @@ void root_first_order(const void* const* srcs, int nranks, int root, const char*
 
 // Launch the plan over buffers given in fold order (the kernels fold
 // ordered[0], ordered[1], ... in index order).
-int run(const Plan& p, const char* const* ordered, void* dst, hipStream_t stream) {
-    if (p.family == kFamNone) return PTORED_OK;
-    int cu = 0;
-    int st = cu_count_of_current_device(cu);
+int run(const Plan& plan, const char* const* ordered, void* dst, hipStream_t stream) {
+    if (plan.family == kFamNone) return PTORED_OK;
+    DeviceFacts f;
+    int st = facts_of_current_device(f);
     if (st != PTORED_OK) return st;
+    const Plan p = with_device(plan, f);
+    const int cu = f.cu;
     (void)hipGetLastError();  // clear a stale error so the check below is ours
 
     KArgs a{};
@@ -410,11 +463,13 @@ int launch_ring(const Plan& p, const RingArgs& a, int cu, hipStream_t s) {
 // launch in all for streams up to 2 GiB).  Every stream is 16-byte aligned,
 // so window offsets that are multiples of 16 keep whole slots whole.
 // `bounds` are the segment boundaries in elements.
-int run_ring(const Plan& p, const void* const* srcs, void* const* dsts, const int64_t* bounds,
+int run_ring(const Plan& plan, const void* const* srcs, void* const* dsts, const int64_t* bounds,
              int64_t count, hipStream_t stream) {
-    int cu = 0;
-    int st = cu_count_of_current_device(cu);
+    DeviceFacts f;
+    int st = facts_of_current_device(f);
     if (st != PTORED_OK) return st;
+    const Plan p = with_device(plan, f);
+    const int cu = f.cu;
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     const int n = p.nranks;
     const int64_t es = p.esize, total = count * es;
@@ -501,6 +556,8 @@ extern "C" int ptored_treduce_plan(const void* const* srcs, int nranks, int root
         info->slots_per_thread = p.unroll;
         info->slots = p.slots;
         info->launches = p.launches;
+        info->wgs_per_cu = p.wgs_per_cu;
+        info->reserved = 0;
     }
     return PTORED_OK;
 }
@@ -572,8 +629,11 @@ extern "C" int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, v
         st = make_plan(ptrs, 2 * nranks, nranks, 1, count, count, dtype, op, tuning, kModeReduce,
                        p);
         if (st != PTORED_OK) return st;
-        if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages)
+        if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages) {
+            if (p.wgs_per_cu > 0)  // the ring kernel moves one slot per thread
+                p.wgs_per_cu = wgs_per_cu_for((uint64_t)(nranks + 1) * kBlock * 16u);
             return run_ring(p, srcs, dsts, bounds, count, stream);
+        }
     }
     const int es = esize_of(dtype);
     for (int s = 0; s < nranks; ++s) {

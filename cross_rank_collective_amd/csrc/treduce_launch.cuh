@@ -14,10 +14,13 @@
 namespace ptored {
 
 // Launch KERNEL over `tiles` tiles.  Default (blocks_per_cu == 0): one
-// block per tile, so the dispatcher hands tiles to whichever CU frees up
-// first -- on MI355X this beat every persistent grid size measured.
-// blocks_per_cu > 0: a persistent grid of that many blocks per CU;
-// blocks_per_cu < 0: a persistent grid at the kernel's occupancy.
+// block per tile, so the dispatcher hands tiles out in order to whichever
+// CU frees up first -- on MI355X this beat every persistent grid size
+// measured -- with p.wgs_per_cu blocks resident per CU: each block reserves
+// p.cap_lds bytes of LDS (its own static LDS included), which it does not
+// use, so that no more fit.  blocks_per_cu > 0: a persistent grid of that
+// many blocks per CU; blocks_per_cu < 0: a persistent grid at the kernel's
+// occupancy.
 template <auto KERNEL, class ARGS>
 static void launch_grid(const Plan& p, const ARGS& a, uint64_t tiles, int cu_count,
                         hipStream_t s) {
@@ -39,7 +42,17 @@ static void launch_grid(const Plan& p, const ARGS& a, uint64_t tiles, int cu_cou
         if (grid > cap) grid = cap;
     }
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(KERNEL, dim3((uint32_t)grid), dim3(kBlock), 0, s, a);
+    uint32_t shmem = 0;
+    if (p.cap_lds > 0 && tiles >= p.cap_min_tiles) {
+        static const uint32_t static_lds = [] {
+            hipFuncAttributes at{};
+            return hipFuncGetAttributes(&at, reinterpret_cast<const void*>(KERNEL)) == hipSuccess
+                       ? (uint32_t)at.sharedSizeBytes
+                       : 0u;
+        }();
+        shmem = p.cap_lds > static_lds ? p.cap_lds - static_lds : 0u;
+    }
+    hipLaunchKernelGGL(KERNEL, dim3((uint32_t)grid), dim3(kBlock), shmem, s, a);
 }
 
 template <auto KERNEL>

@@ -95,6 +95,9 @@ struct Plan {
     bool accumulate;    // push-with-add: dst += every source, by atomics
     bool lds_stages;    // main tiles staged through LDS (ping-pong variant)
     int blocks_per_cu;  // 0: one tile per block; > 0: persistent grid; < 0: at occupancy
+    int wgs_per_cu;     // one tile per block: workgroups kept resident per CU (0 = no limit)
+    uint32_t cap_lds;   // LDS bytes a workgroup reserves to hold that limit (0 = none)
+    uint64_t cap_min_tiles; // launches with fewer tiles run without the limit
     // geometry of the whole call
     int64_t valid_rows;
     int64_t valid_cols;
@@ -116,6 +119,20 @@ constexpr int unroll_for(int nranks) {
     return nranks <= 2 ? 2 : 1;
 }
 constexpr int kElemUnroll = 4;     // elements per thread, element-wise path
+
+// Workgroups kept resident per CU for one-tile-per-block launches, from the
+// HBM bytes one tile moves (reads + writes).  Measured on MI355X over rank
+// counts 2-32, the reduction, the in-place allreduce and the ring: with
+// every CU full (8 workgroups) the chip works on thousands of scattered
+// 1-4 KiB runs at once; keeping only a few tiles per CU resident, issued in
+// order by the dispatcher, keeps the live window of every buffer compact
+// and raised the large reductions 5-12%.  Small tiles want 3, mid-size 2,
+// the largest (runtime rank counts, the allreduce at N >= 12) 1.
+constexpr int wgs_per_cu_for(uint64_t tile_bytes) {
+    return tile_bytes <= 24u * 1024u ? 3 : (tile_bytes <= 96u * 1024u ? 2 : 1);
+}
+// A launch needs this many waves of capped workgroups to be worth capping.
+constexpr int kCapMinRounds = 4;
 constexpr int kLdsStages = 4;      // LDS stages per wave in the ping-pong variant
 constexpr int kRuntimeUnroll = 2;  // slots per thread, runtime rank count
 

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define PTORED_ABI_VERSION 1
+#define PTORED_ABI_VERSION 2
 /* Largest number of ranks (source buffers) one call accepts. */
 #define PTORED_MAX_RANKS 64
 
@@ -123,13 +123,16 @@ int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int
                                          tiles) instead of registers; N >= 2, 16-byte data */
 #define PTORED_SEGMENT_LAUNCHES 0x40u /* reduce-scatter: one launch per ring segment instead of
                                          one launch over every segment */
+#define PTORED_FULL_OCCUPANCY 0x80u   /* let every CU hold as many workgroups as fit, instead of
+                                         the 1-3 per CU the automatic launch keeps resident */
 
 /* Launch choices of ptored_treduce_ex. */
 typedef struct ptored_tuning {
     uint32_t flags;          /* PTORED_FORCE_* and PTORED_NO_XCD_REMAP bits */
-    int32_t blocks_per_cu;   /* 0 = one workgroup per tile (default); > 0 = persistent grid
-                                of that many workgroups per compute unit; < 0 = persistent
-                                grid at the kernel's occupancy */
+    int32_t blocks_per_cu;   /* 0 = one workgroup per tile (default; 1-3 resident per compute
+                                unit, by the bytes a tile moves); > 0 = persistent grid of that
+                                many workgroups per compute unit, in per-XCD bands; < 0 =
+                                persistent grid at the kernel's occupancy */
     int64_t max_launch_bytes; /* split a call into launches that touch at most this many
                                  bytes of each buffer; 0 = auto (2^31) */
 } ptored_tuning;
@@ -154,6 +157,9 @@ typedef struct ptored_plan_info {
     int32_t slots_per_thread; /* slots one thread handles per tile */
     int64_t slots;         /* slots in the whole call */
     int64_t launches;      /* kernel launches the call is split into */
+    int32_t wgs_per_cu;    /* workgroups kept resident per CU by one-tile-per-block
+                              launches large enough to fill them; 0 = as many as fit */
+    int32_t reserved;      /* 0 */
 } ptored_plan_info;
 
 /* Validate like ptored_treduce_ex and describe the launch it would make,

@@ -52,7 +52,7 @@ def test_one_hip_runtime_is_mapped():
 
 
 def test_version_and_limits():
-    assert crc.ptored_abi_version() == 1
+    assert crc.ptored_abi_version() == 2
     assert crc.ptored_max_ranks() == 64
 
 
@@ -127,6 +127,23 @@ def test_plan_paths():
     info = _plan(n=5, srcs=A[:5], tuning=t)
     assert (B.PATHS[info.path], info.slots_per_thread) == ("vec_runtime", 1)
     assert B.PATHS[_plan(n=1, tuning=t).path] == "copy"  # one rank: nothing to stage
+
+
+def test_plan_resident_workgroups():
+    """Workgroups kept resident per CU by one-tile-per-block launches, from
+    the bytes one tile moves: 3 up to 24 KiB, 2 up to 96 KiB, 1 beyond; no
+    limit for the element-wise kernel, persistent grids or on request."""
+    assert _plan(n=16, srcs=A[:16], dtype=3).wgs_per_cu == 2   # 17 x 4 KiB
+    assert _plan(n=8, srcs=A[:8], dtype=1).wgs_per_cu == 2     # 9 x 4 KiB
+    assert _plan(n=5, srcs=A[:5]).wgs_per_cu == 3              # 6 x 4 KiB
+    assert _plan(n=6, srcs=A[:6]).wgs_per_cu == 2              # 7 x 4 KiB
+    assert _plan(n=2, srcs=A[:2]).wgs_per_cu == 3              # 3 x 8 KiB (2 slots per thread)
+    assert _plan(n=1).wgs_per_cu == 3                          # copy: 2 x 8 KiB
+    assert _plan(n=17, srcs=A[:17]).wgs_per_cu == 1            # 18 x 8 KiB
+    assert _plan(srcs=[A[0], A[1] + 4]).wgs_per_cu == 0        # element-wise
+    assert _plan(tuning=B.tuning(flags=B.PTORED_FULL_OCCUPANCY)).wgs_per_cu == 0
+    assert _plan(tuning=B.tuning(blocks_per_cu=2)).wgs_per_cu == 0
+    assert _plan(vr=0).wgs_per_cu == 0
 
 
 def test_plan_walk_and_slots():
