@@ -38,6 +38,7 @@ PTORED_ROW_TILES = 0x10
 PTORED_LDS_PINGPONG = 0x20
 PTORED_SEGMENT_LAUNCHES = 0x40
 PTORED_FULL_OCCUPANCY = 0x80
+PTORED_FLAT_WALK = 0x100
 
 PATHS = {0: "none", 1: "copy", 2: "vec_fixed", 3: "vec_runtime", 4: "elementwise"}
 

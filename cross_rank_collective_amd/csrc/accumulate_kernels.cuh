@@ -72,23 +72,25 @@ __device__ __forceinline__ void atomic_add_elem(char* p, uint32_t bits) {
     }
 }
 
-// Tiles as in treduce_kernel (U = 1): main tiles of 16-byte slots, then row
-// remainders; without VEC, element tiles only.  gridDim.y = N.
+// Tiles as in treduce_kernel (U = 1): row remainders, then main tiles of
+// 16-byte slots; without VEC, element tiles only.  gridDim.y = N.
 template <int DT, int ES, int WALK, bool VEC>
 __global__ __launch_bounds__(kBlock) void accumulate_kernel(const KArgs a) {
     const rsrc_t rs = make_rsrc(a.src[blockIdx.y], a.extent);
     char* const d = static_cast<char*>(a.dst);
     for (uint32_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
         if constexpr (VEC) {
-            if (t < a.main_tiles) {
-                const uint32_t off = slot_offset<WALK>(a, t * (uint32_t)kBlock + threadIdx.x);
+            const uint32_t tails = a.total_tiles - a.main_tiles;  // issued first, as in treduce_kernel
+            if (t >= tails) {
+                const uint32_t off =
+                    slot_offset<WALK>(a, (t - tails) * (uint32_t)kBlock + threadIdx.x);
                 if (off != kOutOfRange) {
                     const u32x4 x = load16(rs, off);
 #pragma unroll
                     for (int w = 0; w < 4; ++w) atomic_add_word<DT>(d + off + 4 * w, x[w]);
                 }
             } else {
-                const uint32_t q = (t - a.main_tiles) * (uint32_t)kBlock + threadIdx.x;
+                const uint32_t q = t * (uint32_t)kBlock + threadIdx.x;
                 if (q < a.ntail) {
                     const uint32_t off = q * a.ld_bytes + a.tail_col_bytes;
                     for (uint32_t e = 0; e < a.tail_bytes; e += ES)

@@ -160,19 +160,20 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
     const int64_t vec = p.vec_elems;
     if (p.rows_mode) {
         p.slots = valid_rows * ((valid_cols + vec - 1) / vec);
-        // Default: the flattened walk.  On request, row tiles -- when a
-        // row's full slots fill its column chunks well (at least 7/8 of the
-        // threads busy, or 8+ chunks per row).  Row tiles keep every wave's
-        // 1 KiB run inside one row and cache-line aligned (no line is
-        // fetched twice), yet on MI355X the flattened walk measured faster
-        // on ragged rows, so it stays the default.
+        // Row tiles when a row's full slots fill its column chunks well (at
+        // least 7/8 of the threads busy, or 8+ chunks per row), else the
+        // flattened walk.  Row tiles keep every wave's 1 KiB run inside one
+        // row and cache-line aligned, so no line is fetched twice; with
+        // few workgroups resident per CU they measured 3-4% faster than the
+        // flattened walk on ragged rows.
         p.rows_mode = kWalkFlat;
-        if (p.family != kFamElem && mode == kModeReduce && !p.lds_stages &&
-            (flags & PTORED_ROW_TILES) != 0) {
+        if (p.family != kFamElem && mode != kModeAccumulate && !p.lds_stages &&
+            (flags & PTORED_FLAT_WALK) == 0) {
             const int64_t full = valid_cols / vec;
             const int64_t per_tile = (int64_t)kBlock * p.unroll;
             const int64_t tiles = (full + per_tile - 1) / per_tile;
-            if (full > 0 && (full * 8 >= tiles * per_tile * 7 || tiles >= 8))
+            const bool fills = full * 8 >= tiles * per_tile * 7 || tiles >= 8;
+            if (full > 0 && (fills || (flags & PTORED_ROW_TILES) != 0))
                 p.rows_mode = kWalkRowTiles;
         }
     } else {

@@ -708,9 +708,11 @@ __device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
     }
 }
 
-// The reduction kernel.  Tiles [0, main_tiles) are main tiles, the rest
-// tail tiles; block b takes tiles b, b + G, ... (one tile per block when
-// G equals the tile count).  NR == 0: runtime rank count.  VEC: 16-byte
+// The reduction kernel.  The first total_tiles - main_tiles tiles are tail
+// tiles (row remainders), the rest main tiles: issued first, the scattered
+// remainder accesses overlap the main tiles' streaming instead of forming a
+// serial phase at the end (measured 3-4% on ragged rows).  Block b takes
+// tiles b, b + G, ... (one tile per block when G equals the tile count).  NR == 0: runtime rank count.  VEC: 16-byte
 // main tiles with row-remainder tails; otherwise element tiles only.
 // WALK: kWalkContig, kWalkRowTiles or kWalkFlat.  ALL: store the result
 // into every source buffer instead of dst (in-place allreduce).
@@ -720,10 +722,11 @@ __global__ __launch_bounds__(kBlock) void treduce_kernel(const KArgs a) {
     for (uint32_t t = logical_block(blockIdx.x, grid, a.xcd_remap != 0u); t < a.total_tiles;
          t += grid) {
         if constexpr (VEC) {
-            if (t < a.main_tiles) {
-                main_tile<DT, OP, NR, U, WALK, ALL>(a, t);
+            const uint32_t tails = a.total_tiles - a.main_tiles;
+            if (t >= tails) {
+                main_tile<DT, OP, NR, U, WALK, ALL>(a, t - tails);
             } else {
-                row_tail_tile<DT, OP, ES, NR, ALL>(a, t - a.main_tiles);
+                row_tail_tile<DT, OP, ES, NR, ALL>(a, t);
             }
         } else {
             element_tile<DT, OP, ES, NR, WALK, ALL>(a, t);
@@ -732,17 +735,18 @@ __global__ __launch_bounds__(kBlock) void treduce_kernel(const KArgs a) {
 }
 
 // The LDS ping-pong kernel: main tiles through LDS stages (one slot per
-// thread), row remainders as in treduce_kernel.  Runtime rank count.
+// thread), row remainders (first) as in treduce_kernel.  Runtime rank count.
 template <int DT, int OP, int ES, int WALK, int S>
 __global__ __launch_bounds__(kBlock) void treduce_lds_kernel(const KArgs a) {
     __shared__ LdsStages<S> stages;
     const uint32_t grid = gridDim.x;
     for (uint32_t t = logical_block(blockIdx.x, grid, a.xcd_remap != 0u); t < a.total_tiles;
          t += grid) {
-        if (t < a.main_tiles) {
-            main_tile_lds<DT, OP, S, WALK>(a, t, stages);
+        const uint32_t tails = a.total_tiles - a.main_tiles;
+        if (t >= tails) {
+            main_tile_lds<DT, OP, S, WALK>(a, t - tails, stages);
         } else {
-            row_tail_tile<DT, OP, ES, 0, false>(a, t - a.main_tiles);
+            row_tail_tile<DT, OP, ES, 0, false>(a, t);
         }
     }
 }

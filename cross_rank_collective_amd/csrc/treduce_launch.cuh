@@ -88,9 +88,10 @@ static int dispatch_n(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
 
 template <int DT, int OP, int ES>
 static int dispatch_op(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
-    if (p.store_all) {  // in-place allreduce: contiguous or flattened walks only
+    if (p.store_all) {  // in-place allreduce
         switch (p.rows_mode) {
         case kWalkContig: return dispatch_n<DT, OP, ES, kWalkContig, true>(p, a, cu, s);
+        case kWalkRowTiles: return dispatch_n<DT, OP, ES, kWalkRowTiles, true>(p, a, cu, s);
         case kWalkFlat: return dispatch_n<DT, OP, ES, kWalkFlat, true>(p, a, cu, s);
         default: return -1;
         }

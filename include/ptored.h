@@ -116,13 +116,15 @@ int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int
 #define PTORED_FORCE_RUNTIME_N 0x4u   /* rank-count loop instead of an unrolled N */
 #define PTORED_NO_XCD_REMAP 0x8u      /* persistent grid: plain block order, not per-XCD bands */
 #define PTORED_ROW_TILES 0x10u        /* 2-D region: tiles of one row's column chunk (the pages'
-                                         2-D sliding chunk walk) instead of slots numbered
-                                         straight through the rows */
+                                         2-D sliding chunk walk, the default when a row's
+                                         slots fill its chunks well) even when they do not */
 #define PTORED_LDS_PINGPONG 0x20u     /* stage the sources through a ring of LDS buffers with
                                          direct buffer-to-LDS loads (the pages' ping/pong
                                          tiles) instead of registers; N >= 2, 16-byte data */
 #define PTORED_SEGMENT_LAUNCHES 0x40u /* reduce-scatter: one launch per ring segment instead of
                                          one launch over every segment */
+#define PTORED_FLAT_WALK 0x100u       /* 2-D region: slots numbered straight through the rows
+                                         instead of row tiles */
 #define PTORED_FULL_OCCUPANCY 0x80u   /* let every CU hold as many workgroups as fit, instead of
                                          the 1-3 per CU the automatic launch keeps resident */
 

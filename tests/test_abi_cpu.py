@@ -152,21 +152,28 @@ def test_plan_walk_and_slots():
     info = _plan(rows=8, cols=10, ld=12, vr=7, vc=10)  # narrow rows: flattened, 3 slots/row
     assert (info.rows_mode, info.slots) == (2, 21)
     info = _plan(rows=8, cols=8, ld=8, vr=8, vc=8, tuning=B.tuning(flags=B.PTORED_FORCE_ROWS))
-    assert (info.rows_mode, info.slots) == (2, 16)
-    # wide rows: flattened by default; row tiles (tile = row x column chunk) on
-    # request: 1000 f32 = 250 slots in one chunk
+    assert (info.rows_mode, info.slots) == (2, 16)  # 2 slots per row fill 1/128 of a chunk
+    # wide rows: row tiles (tile = row x column chunk) when a row's slots fill
+    # its chunks: 1000 f32 = 250 slots in one chunk of 256; flattened on request
     info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000)
-    assert (info.rows_mode, info.slots) == (2, 60 * 250)
-    rt = B.tuning(flags=B.PTORED_ROW_TILES)
-    info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000, tuning=rt)
     assert (info.rows_mode, info.slots) == (1, 60 * 250)
-    # 3 chunks of 256 slots for 513 slots: 513/768 of the threads busy -> flattened
-    info = _plan(n=4, srcs=A[:4], rows=4, cols=2052, ld=2056, vr=4, vc=2052, tuning=rt)
+    flat = B.tuning(flags=B.PTORED_FLAT_WALK)
+    info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000, tuning=flat)
+    assert (info.rows_mode, info.slots) == (2, 60 * 250)
+    # 3 chunks of 256 slots for 513 slots: 513/768 of the threads busy -> flattened,
+    # unless row tiles are forced
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=2052, ld=2056, vr=4, vc=2052)
     assert info.rows_mode == 2
-    # 8 or more chunks per row: row tiles whatever the last chunk holds
-    info = _plan(n=4, srcs=A[:4], rows=4, cols=4 * 7 * 256 + 4, ld=7200, vr=4, vc=7172,
-                 tuning=rt)
+    rt = B.tuning(flags=B.PTORED_ROW_TILES)
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=2052, ld=2056, vr=4, vc=2052, tuning=rt)
     assert info.rows_mode == 1
+    # 8 or more chunks per row: row tiles whatever the last chunk holds
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=4 * 7 * 256 + 4, ld=7200, vr=4, vc=7172)
+    assert info.rows_mode == 1
+    # the LDS variant walks flattened
+    lds = B.tuning(flags=B.PTORED_LDS_PINGPONG)
+    info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000, tuning=lds)
+    assert info.rows_mode == 2
     info = _plan(rows=1, cols=13, ld=16, vr=1, vc=13, dtype=2)  # one row: contiguous f16
     assert (info.rows_mode, info.vec_elems, info.slots) == (0, 8, 2)
 
@@ -188,16 +195,16 @@ def test_workload_plans():
     """Each named workload takes the kernel family its shape calls for."""
     want = {
         "n2_f32_16x16": ("vec_fixed", 0),
-        "n4_f32_1024x1024_valid1000x1000": ("vec_fixed", 2),
+        "n4_f32_1024x1024_valid1000x1000": ("vec_fixed", 1),
         "n8_bf16_8192x8192": ("vec_fixed", 0),
         "n16_i32_4096x4096": ("vec_fixed", 0),
-        "n8_f16_8192x12288_valid8191x12287": ("vec_fixed", 2),
+        "n8_f16_8192x12288_valid8191x12287": ("vec_fixed", 1),
     }
     for name, w in W.WORKLOADS.items():
         info = _plan(n=w.nranks, srcs=A[:w.nranks], rows=w.rows, cols=w.cols, ld=w.ld,
                      vr=w.valid_rows, vc=w.valid_cols, dtype=B.DTYPES[w.dtype],
                      op=B.OPS[w.ops[0]])
-        assert (B.PATHS[info.path], info.rows_mode) == want[name], name  # 2 = flattened
+        assert (B.PATHS[info.path], info.rows_mode) == want[name], name  # 1 = row tiles
         assert info.launches == 1
 
 

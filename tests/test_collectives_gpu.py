@@ -57,8 +57,9 @@ def test_allreduce_in_place_random(dtype):
         vr, vc = int(rng.integers(1, rows + 1)), int(rng.integers(1, cols + 1))
         root = int(rng.integers(0, n))
         op = OPS[case % 4]
-        flags = [0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_FORCE_ROWS,
-                 B.PTORED_FORCE_RUNTIME_N][case % 4]
+        flags = [0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES,
+                 B.PTORED_FORCE_RUNTIME_N, B.PTORED_FORCE_ROWS | B.PTORED_FLAT_WALK,
+                 B.PTORED_FULL_OCCUPANCY][case % 6]
         offs = [0 if case % 3 else int(rng.integers(0, 8)) * es for _ in range(n)]
         size = (rows - 1) * ld + cols
         srcs = [_rand_elems(dtype, rng, size, wild=0.05) for _ in range(n)]

@@ -82,7 +82,9 @@ VARIANTS = [
     ("auto", 0, 0),
     ("elementwise", B.PTORED_FORCE_ELEMENTWISE, 0),
     ("rows", B.PTORED_FORCE_ROWS, 0),
+    ("flat", B.PTORED_FORCE_ROWS | B.PTORED_FLAT_WALK, 0),
     ("row_tiles", B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES, 0),
+    ("full_occupancy", B.PTORED_FULL_OCCUPANCY, 0),
     ("runtime_n", B.PTORED_FORCE_RUNTIME_N, 0),
     ("lds_pingpong", B.PTORED_LDS_PINGPONG, 0),
     ("persistent_noremap", B.PTORED_NO_XCD_REMAP, 2),
@@ -138,7 +140,10 @@ def test_medium_cases_span_many_tiles(dtype):
     rng = np.random.default_rng({"f32": 21, "bf16": 22, "f16": 23, "i32": 24}[dtype])
     for case, (rows, cols, ld, vr, vc) in enumerate(MEDIUM):
         for n, op, vname, flags, bpc in [(4, OPS[case % 4], "auto", 0, 1),
-                                         (9, OPS[(case + 1) % 4], "rows", B.PTORED_FORCE_ROWS, 0),
+                                         (9, OPS[(case + 1) % 4], "flat",
+                                          B.PTORED_FORCE_ROWS | B.PTORED_FLAT_WALK, 0),
+                                         (7, OPS[(case + 2) % 4], "full_occupancy",
+                                          B.PTORED_FULL_OCCUPANCY, 0),
                                          (6, OPS[(case + 1) % 4], "row_tiles",
                                           B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES, 0),
                                          (11, OPS[(case + 2) % 4], "lds_pingpong",
@@ -173,7 +178,7 @@ def test_split_into_many_launches(dtype):
         n = 5
         size = (rows - 1) * ld + cols
         srcs = [_rand_elems(dtype, rng, size, wild=0.02) for _ in range(n)]
-        for flags in (0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_ROW_TILES):
+        for flags in (0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_ROW_TILES, B.PTORED_FLAT_WALK):
             t = B.tuning(flags=flags, max_launch_bytes=mlb)
             st_plan, info = B.ptored_treduce_plan([0x100000] * n, n, 1, 0x900000, rows, cols, ld,
                                                   vr, vc, B.DTYPES[dtype], 0, t)
@@ -289,9 +294,8 @@ def test_workload_full_size(name):
     rng = np.random.default_rng(7)
     full_compare = w.dtype == "i32" or w.buffer_elems <= 1 << 21
     variants = [("auto", 0), ("row_tiles", B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES),
+                ("flat", B.PTORED_FORCE_ROWS | B.PTORED_FLAT_WALK),
                 ("lds_pingpong", B.PTORED_LDS_PINGPONG)]
-    if w.valid_cols == w.ld:
-        variants.append(("rows", B.PTORED_FORCE_ROWS))  # the flattened 2-D walk, same data
     es = w.esize
     for op in w.ops:
         results = []
