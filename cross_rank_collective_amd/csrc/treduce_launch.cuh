@@ -44,13 +44,16 @@ static void launch_grid(const Plan& p, const ARGS& a, uint64_t tiles, int cu_cou
     if (grid < 1) grid = 1;
     uint32_t shmem = 0;
     if (p.cap_lds > 0 && tiles >= p.cap_min_tiles) {
-        static const uint32_t static_lds = [] {
+        // the kernel's own static LDS counts toward the reservation; when it
+        // cannot be read, the launch goes without the limit
+        static const int64_t static_lds = [] {
             hipFuncAttributes at{};
             return hipFuncGetAttributes(&at, reinterpret_cast<const void*>(KERNEL)) == hipSuccess
-                       ? (uint32_t)at.sharedSizeBytes
-                       : 0u;
+                       ? (int64_t)at.sharedSizeBytes
+                       : int64_t(-1);
         }();
-        shmem = p.cap_lds > static_lds ? p.cap_lds - static_lds : 0u;
+        if (static_lds >= 0 && (int64_t)p.cap_lds > static_lds)
+            shmem = p.cap_lds - (uint32_t)static_lds;
     }
     hipLaunchKernelGGL(KERNEL, dim3((uint32_t)grid), dim3(kBlock), shmem, s, a);
 }
