@@ -30,6 +30,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -72,14 +73,23 @@ def traffic_path(workload: str, op: str, mode: str) -> str:
 CSRC = os.path.join(ROOT, "cross_rank_collective_amd", "csrc")
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed (the code
+    in these files has no string literal holding comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources; the stored HBM counter readings are only
-    quoted while the kernels are the ones they were taken on."""
+    """Hash of the library's code (comments and layout ignored); the stored
+    HBM counter readings are only quoted while the code is the one they
+    were taken on."""
     h = hashlib.sha256()
     for fn in sorted(os.listdir(CSRC)):
         if fn.endswith((".cuh", ".hip", ".h", ".cpp")):
             h.update(fn.encode())
-            h.update(open(os.path.join(CSRC, fn), "rb").read())
+            h.update(_code_only(open(os.path.join(CSRC, fn), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,10 +24,12 @@
 //               rectangle, the row found by a multiply-high division.
 // Block b takes tiles b, b+G, b+2G, ... of a grid of G blocks (the pages'
 // block-cyclic walk).  By default G equals the tile count -- one tile per
-// block, so the hardware dispatcher balances the work over the XCDs as
-// blocks retire; a smaller persistent grid can be requested.  Within a
-// tile, wave w owns U * 64 consecutive slots and lane l the slots l, l+64,
-// ..., so every wave instruction moves 1 KiB of one buffer.
+// block, handed out in order by the hardware dispatcher, round-robin over
+// the XCDs, as blocks retire -- and the host keeps only 1-3 blocks resident
+// per CU (an LDS reservation), so the tiles in flight cover a compact
+// window of every buffer; a smaller persistent grid can be requested.
+// Within a tile, wave w owns U * 64 consecutive slots and lane l the slots
+// l, l+64, ..., so every wave instruction moves 1 KiB of one buffer.
 //
 // Per slot a thread issues the loads of all N sources before it combines
 // anything -- the many waves in flight on a CU take the place of the pages'
@@ -43,14 +45,17 @@
 // the extent instead of a branch.  Source loads are non-temporal (the data
 // is used once); stores are device-scope (sc1), which writes through the
 // XCD's L2 to memory -- on MI355X this measured faster for a read-mostly
-// stream than non-temporal or default stores.
+// stream than non-temporal or default stores (the in-place allreduce's N
+// store-backs add nt).
 //
 // Ragged edges.  Full 16-byte slots form the main tiles; the valid bytes
 // after the last full slot of each row (fewer than 16), or at the end of a
-// contiguous span, form separate tail tiles in which one thread moves one
-// row's remainder with at most two exact-size accesses per buffer (12 + 2
-// bytes for seven 16-bit elements), so nothing outside the valid rectangle
-// is touched.  The main tiles are therefore branch-free.  The element-wise
+// contiguous span, form separate tail tiles -- placed before the main tiles
+// in the grid, so their scattered accesses overlap the streaming -- in
+// which one thread moves one row's remainder with at most two exact-size
+// accesses per buffer (12 + 2 bytes for seven 16-bit elements), so nothing
+// outside the valid rectangle is touched.  The main tiles are therefore
+// branch-free.  The element-wise
 // path (data not 16-byte aligned) has no main tiles: its tail tiles carry
 // every element of the rectangle, one element per access.
 //
