@@ -381,6 +381,16 @@ def main() -> int:
     torch.cuda.synchronize(dev)
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
+    # Per-step distribution, from a second pass with an event pair around
+    # every step (not part of `value`, which is the run above).
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for a_ev, b_ev in marks:
+        a_ev.record(stream)
+        step()
+        b_ev.record(stream)
+    torch.cuda.synchronize(dev)
+    per_step = sorted(a_ev.elapsed_time(b_ev) for a_ev, b_ev in marks)
     gbs = algo_bytes / (ms_step * 1e-3) / 1e9
     elems_s = w.valid_rows * w.valid_cols / (ms_step * 1e-3)
 
@@ -393,6 +403,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 5),
+                    "min": round(per_step[0], 5), "max": round(per_step[-1], 5)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
