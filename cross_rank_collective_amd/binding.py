@@ -52,7 +52,7 @@ class ptored_plan_info(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("rows_mode", ctypes.c_int32),
                 ("vec_elems", ctypes.c_int32), ("slots_per_thread", ctypes.c_int32),
                 ("slots", ctypes.c_int64), ("launches", ctypes.c_int64),
-                ("wgs_per_cu", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("wgs_per_cu", ctypes.c_int32), ("lead", ctypes.c_int32)]
 
 
 class PtoredError(RuntimeError):

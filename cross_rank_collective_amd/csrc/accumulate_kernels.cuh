@@ -72,8 +72,8 @@ __device__ __forceinline__ void atomic_add_elem(char* p, uint32_t bits) {
     }
 }
 
-// Tiles as in treduce_kernel (U = 1): row remainders, then main tiles of
-// 16-byte slots; without VEC, element tiles only.  gridDim.y = N.
+// Tiles as in treduce_kernel (U = 1): row remainders and heads, then main
+// tiles of 16-byte slots; without VEC, element tiles only.  gridDim.y = N.
 template <int DT, int ES, int WALK, bool VEC>
 __global__ __launch_bounds__(kBlock) void accumulate_kernel(const KArgs a) {
     const rsrc_t rs = make_rsrc(a.src[blockIdx.y], a.extent);
@@ -91,9 +91,13 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const KArgs a) {
                 }
             } else {
                 const uint32_t q = t * (uint32_t)kBlock + threadIdx.x;
-                if (q < a.ntail) {
+                if (q < a.ntail) {  // row remainder
                     const uint32_t off = q * a.ld_bytes + a.tail_col_bytes;
                     for (uint32_t e = 0; e < a.tail_bytes; e += ES)
+                        atomic_add_elem<DT, ES>(d + off + e, load_elem<ES>(rs, off + e));
+                } else if (q - a.ntail < a.nhead) {  // row head: bytes [head_lo, 16)
+                    const uint32_t off = (q - a.ntail) * a.ld_bytes;
+                    for (uint32_t e = a.head_lo; e < 16u; e += ES)
                         atomic_add_elem<DT, ES>(d + off + e, load_elem<ES>(rs, off + e));
                 }
             }

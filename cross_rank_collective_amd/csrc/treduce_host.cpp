@@ -77,8 +77,6 @@ int check_pairs(const void* const* a, int na, const void* const* b, int nb, int6
     return PTORED_OK;
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
 enum Mode { kModeReduce, kModeAllreduce, kModeAccumulate };
 
 // Choose the kernel family and the slot geometry ([TREDUCE] §4.1 analog) for
@@ -119,9 +117,21 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
     p.rows_mode = contiguous ? 0 : 1;
     p.total_elems = contiguous ? (valid_rows == 1 ? valid_cols : valid_rows * ld) : 0;
 
+    // The 16-byte vector path needs every buffer to start at the same byte
+    // offset within a 16-byte block (`lead`; 0 when all are aligned), every
+    // row start to keep it (pitch a multiple of 16 bytes), and, when lead >
+    // 0, every valid row (or the span) to reach the next 16-byte boundary so
+    // that its head is exactly bytes [lead, 16) of its first block.
     bool use_vec = (flags & PTORED_FORCE_ELEMENTWISE) == 0;
-    for (int r = 0; r < nptrs && use_vec; ++r) use_vec = aligned16(ptrs[r]);
+    const uintptr_t lead = reinterpret_cast<uintptr_t>(ptrs[0]) & 15u;
+    for (int r = 1; r < nptrs && use_vec; ++r)
+        use_vec = (reinterpret_cast<uintptr_t>(ptrs[r]) & 15u) == lead;
     if (use_vec && p.rows_mode && ((ld * p.esize) & 15) != 0) use_vec = false;
+    if (use_vec && lead != 0) {
+        const int64_t row_bytes = (contiguous ? p.total_elems : valid_cols) * p.esize;
+        if ((int64_t)lead + row_bytes < 16) use_vec = false;
+    }
+    p.lead = use_vec ? (int)lead : 0;
 
     if (use_vec) {
         p.vec_elems = 16 / p.esize;
@@ -169,7 +179,7 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         p.rows_mode = kWalkFlat;
         if (p.family != kFamElem && mode != kModeAccumulate && !p.lds_stages &&
             (flags & PTORED_FLAT_WALK) == 0) {
-            const int64_t full = valid_cols / vec;
+            const int64_t full = (p.lead + valid_cols * p.esize) / 16 - (p.lead > 0 ? 1 : 0);
             const int64_t per_tile = (int64_t)kBlock * p.unroll;
             const int64_t tiles = (full + per_tile - 1) / per_tile;
             const bool fills = full * 8 >= tiles * per_tile * 7 || tiles >= 8;
@@ -179,19 +189,18 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
     } else {
         p.slots = (p.total_elems + vec - 1) / vec;
     }
-    // Count launches (the same bands run() walks).
+    // Count launches (the same runs and bands run() walks).
     int64_t launches = 0;
-    const int64_t es = p.esize;
+    const int64_t es = p.esize, win = p.max_launch_bytes;
+    const int64_t row_end = p.lead + valid_cols * es;
     if (!p.rows_mode) {
-        const int64_t per = p.max_launch_bytes / es;
-        launches = (p.total_elems + per - 1) / per;
-    } else if (valid_cols * es <= p.max_launch_bytes) {
+        launches = (p.lead + p.total_elems * es + win - 1) / win;
+    } else if (row_end <= win) {
         const int64_t ldb = ld * es;
-        const int64_t rpl = (p.max_launch_bytes - valid_cols * es) / ldb + 1;
+        const int64_t rpl = (win - row_end) / ldb + 1;
         launches = (valid_rows + rpl - 1) / rpl;
     } else {
-        const int64_t per = p.max_launch_bytes / es;
-        launches = valid_rows * ((valid_cols + per - 1) / per);
+        launches = valid_rows * ((row_end + win - 1) / win);
     }
     p.launches = launches;
     return PTORED_OK;
@@ -221,37 +230,45 @@ void finish_tiles(const Plan& p, KArgs& a) {
     const uint64_t per_main = (uint64_t)kBlock * p.unroll;
     const uint64_t per_tail = (uint64_t)kBlock * (p.family == kFamElem ? kElemUnroll : 1);
     a.main_tiles = (uint32_t)((a.nslots + per_main - 1) / per_main);
-    a.total_tiles = a.main_tiles + (uint32_t)((a.ntail + per_tail - 1) / per_tail);
+    a.total_tiles =
+        a.main_tiles + (uint32_t)(((uint64_t)a.ntail + a.nhead + per_tail - 1) / per_tail);
 }
 
-// One launch over a contiguous run of `elems` elements starting at byte
-// offset `byte_off` of every buffer: full 16-byte slots, then the remainder
-// (every element on the element-wise path).
-int launch_span(const Plan& p, KArgs a, const char* const* ordered, char* dst, int64_t byte_off,
-                int64_t elems, int cu, hipStream_t s) {
-    for (int r = 0; r < p.nranks; ++r) a.src[r] = ordered[r] + byte_off;
-    a.dst = dst + byte_off;
-    a.extent = (uint32_t)(elems * p.esize);
+// One launch over bytes [lo, hi) of every buffer, counted from byte `base`
+// of each (its launch base).  Vector path: the base is 16-byte aligned and
+// lo < 16; bytes [lo, 16) form a head when lo > 0, then full 16-byte slots,
+// then the remainder after the last full slot.  Element-wise path: lo == 0,
+// every element is a tail item.
+int launch_span(const Plan& p, KArgs a, const char* const* ordered, char* dst, int64_t base,
+                int64_t lo, int64_t hi, int cu, hipStream_t s) {
+    for (int r = 0; r < p.nranks; ++r) a.src[r] = ordered[r] + base;
+    a.dst = dst + base;
+    a.extent = (uint32_t)hi;
     a.ld_bytes = 0;
     a.div_slots = fast_div_for(1);
     a.div_tail = fast_div_for(1);
     a.tiles_per_row = 1;
     a.div_tiles = fast_div_for(1);
+    a.nhead = 0;
+    a.head_lo = 0;
+    a.slot0_bytes = 0;
     if (p.family == kFamElem) {
+        const int64_t elems = (hi - lo) / p.esize;
         a.nslots = 0;
         a.ntail = (uint32_t)elems;
         a.tail_per_row = (uint32_t)elems;
         a.tail_bytes = 0;
-        a.tail_col_bytes = 0;
+        a.tail_col_bytes = (uint32_t)lo;
     } else {
-        const int64_t vec = p.vec_elems;
-        const int64_t full = elems / vec;
-        const int64_t rem = elems - full * vec;
-        a.nslots = (uint32_t)full;
-        a.ntail = rem > 0 ? 1u : 0u;
+        const int64_t first = (lo + 15) / 16 * 16, last = hi / 16 * 16;
+        a.slot0_bytes = (uint32_t)first;
+        a.nslots = (uint32_t)((last - first) / 16);
+        a.nhead = lo % 16 != 0 ? 1u : 0u;
+        a.head_lo = (uint32_t)(lo % 16);
+        a.ntail = hi > last ? 1u : 0u;
         a.tail_per_row = 0;
-        a.tail_bytes = (uint32_t)(rem * p.esize);
-        a.tail_col_bytes = (uint32_t)(full * 16);
+        a.tail_bytes = (uint32_t)(hi - last);
+        a.tail_col_bytes = (uint32_t)last;
     }
     a.slots_per_row = a.nslots;
     finish_tiles(p, a);
@@ -260,16 +277,36 @@ int launch_span(const Plan& p, KArgs a, const char* const* ordered, char* dst, i
     return launch_one(q, a, cu, s);
 }
 
+// Launches over one run of bytes [lo, hi) counted from 16-byte aligned
+// launch bases (lo < 16), cut into windows of at most max_launch_bytes
+// whose starts stay on the 16-byte grid.
+int launch_run(const Plan& p, const KArgs& a, const char* const* ordered, char* dst,
+               int64_t base, int64_t lo, int64_t hi, int cu, hipStream_t s) {
+    int rc = 0;
+    for (int64_t w0 = 0; w0 < hi && rc == 0; w0 += p.max_launch_bytes) {
+        const int64_t l = std::max(lo, w0) - w0;
+        const int64_t h = std::min(hi, w0 + p.max_launch_bytes) - w0;
+        rc = launch_span(p, a, ordered, dst, base + w0, l, h, cu, s);
+    }
+    return rc;
+}
+
 // One launch over `nrows` rows of the valid rectangle starting at row `row0`.
+// Vector path: each row's valid bytes are [lead, lead + valid_cols * esize)
+// from its (16-byte aligned) start -- a head when lead > 0, full slots, a
+// remainder.
 int launch_rows(const Plan& p, KArgs a, const char* const* ordered, char* dst, int64_t row0,
                 int64_t nrows, int cu, hipStream_t s) {
     const int64_t byte_off = row0 * p.ld * p.esize;
     for (int r = 0; r < p.nranks; ++r) a.src[r] = ordered[r] + byte_off;
     a.dst = dst + byte_off;
-    a.extent = (uint32_t)(((nrows - 1) * p.ld + p.valid_cols) * p.esize);
+    a.extent = (uint32_t)((nrows - 1) * p.ld * p.esize + p.lead + p.valid_cols * p.esize);
     a.ld_bytes = nrows > 1 ? (uint32_t)(p.ld * p.esize) : 0u;
     a.tiles_per_row = 1;
     a.div_tiles = fast_div_for(1);
+    a.nhead = 0;
+    a.head_lo = 0;
+    a.slot0_bytes = 0;
     if (p.family == kFamElem) {
         a.nslots = 0;
         a.slots_per_row = 0;
@@ -280,17 +317,20 @@ int launch_rows(const Plan& p, KArgs a, const char* const* ordered, char* dst, i
         a.tail_bytes = 0;
         a.tail_col_bytes = 0;
     } else {
-        const int64_t vec = p.vec_elems;
-        const int64_t full = p.valid_cols / vec;         // full slots per row
-        const int64_t rem = p.valid_cols - full * vec;   // remainder elements per row
+        const int64_t end = p.lead + p.valid_cols * p.esize;  // row bytes from its start
+        const int64_t first = (p.lead + 15) / 16 * 16, last = end / 16 * 16;
+        const int64_t full = (last - first) / 16;              // full slots per row
+        a.slot0_bytes = (uint32_t)first;
         a.slots_per_row = (uint32_t)full;
         a.nslots = (uint32_t)(full * nrows);
         a.div_slots = fast_div_for(full > 0 ? (uint32_t)full : 1u);
-        a.ntail = rem > 0 ? (uint32_t)nrows : 0u;
+        a.nhead = p.lead > 0 ? (uint32_t)nrows : 0u;
+        a.head_lo = (uint32_t)p.lead;
+        a.ntail = end > last ? (uint32_t)nrows : 0u;
         a.tail_per_row = 0;
         a.div_tail = fast_div_for(1);
-        a.tail_bytes = (uint32_t)(rem * p.esize);
-        a.tail_col_bytes = (uint32_t)(full * 16);
+        a.tail_bytes = (uint32_t)(end - last);
+        a.tail_col_bytes = (uint32_t)last;
     }
     finish_tiles(p, a);
     if (p.rows_mode == kWalkRowTiles) {
@@ -387,28 +427,27 @@ int run(const Plan& plan, const char* const* ordered, void* dst, hipStream_t str
     KArgs a{};
     a.nranks = (uint32_t)p.nranks;
     a.xcd_remap = p.xcd_remap ? 1u : 0u;
-    char* d = static_cast<char*>(dst);
+    // Vector path over buffers that all start `lead` bytes past a 16-byte
+    // boundary: address them from that boundary.
+    const char* base[PTORED_MAX_RANKS];
+    for (int r = 0; r < p.nranks; ++r) base[r] = ordered[r] - p.lead;
+    char* d = static_cast<char*>(dst) - p.lead;
     const int64_t es = p.esize;
+    const int64_t row_end = p.lead + p.valid_cols * es;  // a valid row's bytes from its base
     int rc = 0;
     if (!p.rows_mode) {
         // One contiguous span, cut into launches of at most max_launch_bytes.
-        const int64_t per = p.max_launch_bytes / es;
-        for (int64_t e0 = 0; e0 < p.total_elems && rc == 0; e0 += per)
-            rc = launch_span(p, a, ordered, d, e0 * es, std::min(per, p.total_elems - e0), cu,
-                             stream);
-    } else if (p.valid_cols * es <= p.max_launch_bytes) {
+        rc = launch_run(p, a, base, d, 0, p.lead, p.lead + p.total_elems * es, cu, stream);
+    } else if (row_end <= p.max_launch_bytes) {
         // Row bands whose byte extent fits in 32-bit offsets.
         const int64_t ldb = p.ld * es;
-        const int64_t rpl = (p.max_launch_bytes - p.valid_cols * es) / ldb + 1;
+        const int64_t rpl = (p.max_launch_bytes - row_end) / ldb + 1;
         for (int64_t r0 = 0; r0 < p.valid_rows && rc == 0; r0 += rpl)
-            rc = launch_rows(p, a, ordered, d, r0, std::min(rpl, p.valid_rows - r0), cu, stream);
+            rc = launch_rows(p, a, base, d, r0, std::min(rpl, p.valid_rows - r0), cu, stream);
     } else {
-        // Rows longer than one launch: every row is a contiguous span.
-        const int64_t per = p.max_launch_bytes / es;
+        // Rows longer than one launch: every row is a run of its own.
         for (int64_t r = 0; r < p.valid_rows && rc == 0; ++r)
-            for (int64_t c0 = 0; c0 < p.valid_cols && rc == 0; c0 += per)
-                rc = launch_span(p, a, ordered, d, (r * p.ld + c0) * es,
-                                 std::min(per, p.valid_cols - c0), cu, stream);
+            rc = launch_run(p, a, base, d, r * p.ld * es, p.lead, row_end, cu, stream);
     }
     if (rc != 0) return PTORED_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return PTORED_ERR_HIP;
@@ -558,7 +597,7 @@ extern "C" int ptored_treduce_plan(const void* const* srcs, int nranks, int root
         info->slots = p.slots;
         info->launches = p.launches;
         info->wgs_per_cu = p.wgs_per_cu;
-        info->reserved = 0;
+        info->lead = p.lead;
     }
     return PTORED_OK;
 }
@@ -630,7 +669,8 @@ extern "C" int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, v
         st = make_plan(ptrs, 2 * nranks, nranks, 1, count, count, dtype, op, tuning, kModeReduce,
                        p);
         if (st != PTORED_OK) return st;
-        if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages) {
+        if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages &&
+            p.lead == 0) {
             if (p.wgs_per_cu > 0)  // the ring kernel moves one slot per thread
                 p.wgs_per_cu = wgs_per_cu_for((uint64_t)(nranks + 1) * kBlock * 16u);
             return run_ring(p, srcs, dsts, bounds, count, stream);

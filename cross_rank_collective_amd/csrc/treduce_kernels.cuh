@@ -388,6 +388,46 @@ __device__ __forceinline__ void store_partial(rsrc_t r, uint32_t off, u32x4 v) {
     }
 }
 
+// Bytes [LO, 16) of a 16-byte slot (LO a multiple of 2, 0 < LO < 16) in
+// naturally aligned pieces -- 2 bytes at LO when LO is 2 mod 4, then 4 bytes
+// to reach an 8-byte boundary, then 8 -- into the same words of a vector as
+// a whole slot would fill; the bytes before LO are zero.
+template <int LO>
+__device__ __forceinline__ u32x4 load_head(rsrc_t r, uint32_t off) {
+    static_assert(LO > 0 && LO < 16 && LO % 2 == 0, "head range");
+    u32x4 v = {0u, 0u, 0u, 0u};
+    constexpr int A = (LO + 3) / 4 * 4;  // first 4-byte boundary at or after LO
+    if constexpr (LO % 4 == 2) {
+        v[LO / 4] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off + LO, 0, kLoadPolicy)
+                    << 16;
+    }
+    if constexpr (A == 4 || A == 12) {
+        v[A / 4] = __builtin_amdgcn_raw_buffer_load_b32(r, off + A, 0, kLoadPolicy);
+    }
+    if constexpr (A <= 8) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, off + 8, 0, kLoadPolicy);
+        v[2] = w[0];
+        v[3] = w[1];
+    }
+    return v;
+}
+template <int LO, int POL = kStorePolicy>
+__device__ __forceinline__ void store_head(rsrc_t r, uint32_t off, u32x4 v) {
+    constexpr int A = (LO + 3) / 4 * 4;
+    if constexpr (LO % 4 == 2) {
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[LO / 4] >> 16), r, off + LO, 0,
+                                             POL);
+    }
+    if constexpr (A == 4 || A == 12) {
+        __builtin_amdgcn_raw_buffer_store_b32(v[A / 4], r, off + A, 0, POL);
+    }
+    if constexpr (A <= 8) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = {v[2], v[3]};
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, off + 8, 0, POL);
+    }
+}
+
 // Quotient by a per-launch constant without a divide: the multiply-high
 // method of Granlund and Montgomery ("Division by invariant integers using
 // multiplication", PLDI 1994, Fig. 4.1), exact for every 32-bit dividend.
@@ -411,9 +451,9 @@ __device__ __forceinline__ uint32_t slot_offset(const KArgs& a, uint32_t s) {
     if (s >= a.nslots) return kOutOfRange;
     if constexpr (WALK == kWalkFlat) {
         const uint32_t row = fast_div(s, a.div_slots);
-        return row * a.ld_bytes + (s - row * a.slots_per_row) * 16u;
+        return row * a.ld_bytes + a.slot0_bytes + (s - row * a.slots_per_row) * 16u;
     } else {
-        return s * 16u;
+        return a.slot0_bytes + s * 16u;
     }
 }
 
@@ -531,7 +571,7 @@ __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
     if constexpr (WALK == kWalkRowTiles) {
         const uint32_t row = fast_div(t, a.div_tiles);
         const uint32_t v0 = (t - row * a.tiles_per_row) * (uint32_t)(kBlock * U) + in_tile;
-        const uint32_t row_off = row * a.ld_bytes;
+        const uint32_t row_off = row * a.ld_bytes + a.slot0_bytes;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t v = v0 + (uint32_t)(u * 64);
@@ -703,11 +743,56 @@ __device__ __forceinline__ void row_tail(const KArgs& a, uint32_t off) {
     }
 }
 
-// One tail tile of the vector path: kBlock row remainders, one per thread.
+// One row head: bytes [LO, 16) of the slot at `off`, loaded from every
+// source with the pieces of load_head, folded word-wise in the same order
+// as the main tiles (the zero bytes before LO fold among themselves and are
+// never stored), stored with the same pieces.
+template <int DT, int OP, int NR, int LO, bool ALL>
+__device__ __forceinline__ void row_head(const KArgs& a, uint32_t off) {
+    Acc<DT, OP> acc[4];
+    {
+        const u32x4 x0 = load_head<LO>(make_rsrc(a.src[0], a.extent), off);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[w].init(x0[w]);
+    }
+    const uint32_t n = NR > 0 ? (uint32_t)NR : a.nranks;
+    for (uint32_t k = 1; k < n; ++k) {
+        const u32x4 x = load_head<LO>(make_rsrc(a.src[k], a.extent), off);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[w].add(x[w]);
+    }
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) out[w] = acc[w].get();
+    if constexpr (ALL) {
+        for (uint32_t k = 0; k < n; ++k)
+            store_head<LO, kStoreAllPolicy>(make_rsrc(a.src[k], a.extent), off, out);
+    } else {
+        store_head<LO>(make_rsrc(a.dst, a.extent), off, out);
+    }
+}
+
+// One tail tile of the vector path: kBlock items, one per thread -- row
+// remainders (items [0, ntail)), then row heads (items [ntail, ntail + nhead)).
 template <int DT, int OP, int ES, int NR, bool ALL>
 __device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
     const uint32_t q = t * (uint32_t)kBlock + threadIdx.x;
-    if (q >= a.ntail) return;
+    if (q >= a.ntail) {
+        const uint32_t h = q - a.ntail;
+        if (h >= a.nhead) return;
+        const uint32_t off = h * a.ld_bytes;
+        switch (a.head_lo) {  // uniform over the launch
+        case 2: if constexpr (ES == 2) row_head<DT, OP, NR, 2, ALL>(a, off); break;
+        case 4: row_head<DT, OP, NR, 4, ALL>(a, off); break;
+        case 6: if constexpr (ES == 2) row_head<DT, OP, NR, 6, ALL>(a, off); break;
+        case 8: row_head<DT, OP, NR, 8, ALL>(a, off); break;
+        case 10: if constexpr (ES == 2) row_head<DT, OP, NR, 10, ALL>(a, off); break;
+        case 12: row_head<DT, OP, NR, 12, ALL>(a, off); break;
+        case 14: if constexpr (ES == 2) row_head<DT, OP, NR, 14, ALL>(a, off); break;
+        default: break;
+        }
+        return;
+    }
     const uint32_t off = q * a.ld_bytes + a.tail_col_bytes;
     switch (a.tail_bytes) {  // uniform over the launch
     case 2: if constexpr (ES == 2) row_tail<DT, OP, NR, 2, ALL>(a, off); break;
@@ -725,8 +810,9 @@ __device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
 // tiles (row remainders), the rest main tiles: issued first, the scattered
 // remainder accesses overlap the main tiles' streaming instead of forming a
 // serial phase at the end (measured 3-4% on ragged rows).  Block b takes
-// tiles b, b + G, ... (one tile per block when G equals the tile count).  NR == 0: runtime rank count.  VEC: 16-byte
-// main tiles with row-remainder tails; otherwise element tiles only.
+// tiles b, b + G, ... (one tile per block when G equals the tile count).
+// NR == 0: runtime rank count.  VEC: 16-byte main tiles with row-remainder
+// and row-head tail tiles; otherwise element tiles only.
 // WALK: kWalkContig, kWalkRowTiles or kWalkFlat.  ALL: store the result
 // into every source buffer instead of dst (in-place allreduce).
 template <int DT, int OP, int ES, int NR, int U, int WALK, bool VEC, bool ALL>

@@ -20,7 +20,11 @@ struct FastDiv {
     uint32_t sh2;
 };
 
-// Kernel arguments of one launch (passed by value; ~620 bytes of kernarg).
+// Kernel arguments of one launch (passed by value; ~630 bytes of kernarg).
+// Offsets are bytes from each buffer's launch base, which is 16-byte aligned
+// on the vector path: when every buffer starts the same number of bytes past
+// a 16-byte boundary, the bases are moved back to that boundary and each row
+// begins with a head.
 struct KArgs {
     // src[0] is the root's buffer, then the other ranks in ascending order:
     // the kernels fold src[0], src[1], ... in index order.
@@ -38,6 +42,9 @@ struct KArgs {
     uint32_t tail_bytes;     // bytes of every row remainder (vector path), < 16
     uint32_t tail_col_bytes; // byte offset in a row (or the span) of the remainder
     uint32_t tiles_per_row;  // column chunks per row (row tiles)
+    uint32_t slot0_bytes;    // byte offset of a row's first full slot (16 with a head, else 0)
+    uint32_t nhead;          // head items: a row's bytes before its first full slot
+    uint32_t head_lo;        // a head covers bytes [head_lo, 16) of its row's first slot
     FastDiv div_tiles;       // division by tiles_per_row
     FastDiv div_slots;       // division by slots_per_row
     FastDiv div_tail;        // division by tail_per_row
@@ -94,6 +101,7 @@ struct Plan {
     bool store_all;     // in-place allreduce: the result goes back into every source
     bool accumulate;    // push-with-add: dst += every source, by atomics
     bool lds_stages;    // main tiles staged through LDS (ping-pong variant)
+    int lead;           // vector path: bytes every buffer starts past a 16-byte boundary
     int blocks_per_cu;  // 0: one tile per block; > 0: persistent grid; < 0: at occupancy
     int wgs_per_cu;     // one tile per block: workgroups kept resident per CU (0 = no limit)
     uint32_t cap_lds;   // LDS bytes a workgroup reserves to hold that limit (0 = none)

@@ -104,7 +104,11 @@ typedef enum ptored_status {
  * UNSUPPORTED (dtype or op outside the enums), INVALID_ARG (a pointer not
  * aligned to the element size), OVERLAP.  ERR_HIP is returned when the
  * launch fails.  Pointers or row pitches that are not 16-byte aligned are
- * not errors: they select an element-wise kernel.
+ * not errors.  When every buffer starts at the same offset within a 16-byte
+ * block, the pitch is a multiple of 16 bytes and every valid row reaches the
+ * next 16-byte boundary, the 16-byte vector kernels still run (each row's
+ * bytes before that boundary folded as a head); otherwise misaligned data
+ * selects an element-wise kernel.
  */
 int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int64_t rows,
                    int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
@@ -161,7 +165,8 @@ typedef struct ptored_plan_info {
     int64_t launches;      /* kernel launches the call is split into */
     int32_t wgs_per_cu;    /* workgroups kept resident per CU by one-tile-per-block
                               launches large enough to fill them; 0 = as many as fit */
-    int32_t reserved;      /* 0 */
+    int32_t lead;          /* vector path: bytes past a 16-byte boundary at which every
+                              buffer starts (each row then begins with a head) */
 } ptored_plan_info;
 
 /* Validate like ptored_treduce_ex and describe the launch it would make,

@@ -146,6 +146,31 @@ def test_plan_resident_workgroups():
     assert _plan(vr=0).wgs_per_cu == 0
 
 
+def test_plan_common_lead():
+    """Buffers that all start the same number of bytes past a 16-byte boundary
+    keep the vector path (rows begin with a head); a different offset, a
+    pitch off the 16-byte grid, or a row too short to reach the boundary
+    select the element-wise kernel."""
+    co = [A[0] + 4, A[1] + 4]
+    info = _plan(srcs=co, dst=D + 4)                               # 16 contiguous f32
+    assert (B.PATHS[info.path], info.lead, info.launches) == ("vec_fixed", 4, 1)
+    info = _plan(srcs=co, dst=D + 8)                               # dst at another offset
+    assert (B.PATHS[info.path], info.lead) == ("elementwise", 0)
+    info = _plan(srcs=[A[0] + 6, A[1] + 6], dst=D + 6, dtype=2, rows=8, cols=10, ld=16,
+                 vr=7, vc=9)                                       # f16 rows of 32 B pitch
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 6)
+    info = _plan(srcs=[A[0] + 6, A[1] + 6], dst=D + 6, dtype=2, rows=8, cols=10, ld=12,
+                 vr=7, vc=9)                                       # 24 B pitch
+    assert B.PATHS[info.path] == "elementwise"
+    info = _plan(srcs=[A[0] + 12, A[1] + 12], dst=D + 12, rows=1, cols=1, ld=1, vr=1, vc=1)
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 12)   # exactly [12, 16)
+    info = _plan(srcs=[A[0] + 8, A[1] + 8], dst=D + 8, rows=1, cols=1, ld=1, vr=1, vc=1)
+    assert B.PATHS[info.path] == "elementwise"                     # [8, 12) never reaches 16
+    # windows stay on the 16-byte grid: 4 + 64 bytes in windows of 32
+    info = _plan(srcs=co, dst=D + 4, tuning=B.tuning(max_launch_bytes=32))
+    assert info.launches == 3
+
+
 def test_plan_walk_and_slots():
     info = _plan(rows=8, cols=8, ld=8, vr=8, vc=8)  # contiguous f32
     assert (info.rows_mode, info.vec_elems, info.slots, info.launches) == (0, 4, 16, 1)

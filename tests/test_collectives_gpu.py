@@ -81,6 +81,74 @@ def test_allreduce_in_place_random(dtype):
             assert b.guards_intact()
 
 
+@pytest.mark.parametrize("dtype", DT)
+def test_collectives_common_lead(dtype):
+    """Allreduce, ring reduce-scatter and push-with-add over buffers that all
+    start the same number of bytes past a 16-byte boundary."""
+    rng = np.random.default_rng({"f32": 61, "bf16": 62, "f16": 63, "i32": 64}[dtype])
+    es = ESIZE[dtype]
+    for case in range(8):
+        lead = int(rng.choice(list(range(es, 16, es))))
+        n = int(rng.choice([2, 5, 8, 16]))
+        rows, cols = int(rng.integers(2, 30)), int(rng.integers(16, 900))
+        ld = cols + (-cols) % 8 + 8 * int(rng.integers(0, 2))
+        vr, vc = int(rng.integers(1, rows + 1)), int(rng.integers(8, cols + 1))
+        size = (rows - 1) * ld + cols
+        op = OPS[case % 4]
+        offs = [lead + 16 * int(rng.integers(0, 3)) for _ in range(n)]
+        say(f"lead collectives#{case} {dtype} {op} lead={lead} N={n} {rows}x{cols} ld={ld} "
+            f"valid={vr}x{vc}")
+        # allreduce in place
+        srcs = [_rand_elems(dtype, rng, size, wild=0.05) for _ in range(n)]
+        bufs = _upload(srcs, offs)
+        st = B.ptored_allreduce([b.ptr for b in bufs], n, case % n, rows, cols, ld, vr, vc,
+                                B.DTYPES[dtype], B.OPS[op], None, _stream())
+        torch.cuda.synchronize()
+        assert st == 0, B.ptored_status_string(st)
+        want = [x.copy() for x in srcs]
+        oracle.allreduce_inplace(want, root=case % n, dtype=dtype, op=op, rows=rows, cols=cols,
+                                 ld=ld, valid_rows=vr, valid_cols=vc)
+        for b, w_ in zip(bufs, want):
+            assert compare(dtype, b.download(dtype), w_).all(), case
+            assert b.guards_intact()
+        # ring reduce-scatter over the whole stream
+        count = size
+        sb = _upload(srcs, offs)
+        db = [DevBuf(count * es, lead + 16 * int(rng.integers(0, 3)), fill=0xFF)
+              for _ in range(n)]
+        st = B.ptored_reduce_scatter_ring([b.ptr for b in sb], n, [b.ptr for b in db], count,
+                                          B.DTYPES[dtype], B.OPS[op], None, _stream())
+        torch.cuda.synchronize()
+        assert st == 0, B.ptored_status_string(st)
+        want = [sentinel(dtype, count) for _ in range(n)]
+        oracle.reduce_scatter_ring([x.copy() for x in srcs], want, count=count, dtype=dtype,
+                                   op=op)
+        for b, w_ in zip(db, want):
+            assert compare(dtype, b.download(dtype), w_).all(), case
+            assert b.guards_intact()
+        # push-with-add (i32 exact; floats within the bound of N additions)
+        fsrcs = [_finite_values(dtype, rng, size) for _ in range(n)]
+        d0 = _finite_values(dtype, rng, size)
+        sb = _upload(fsrcs, offs)
+        dd = _upload([d0], [lead])[0]
+        st = B.ptored_accumulate_add([b.ptr for b in sb], n, dd.ptr, rows, cols, ld, vr, vc,
+                                     B.DTYPES[dtype], None, _stream())
+        torch.cuda.synchronize()
+        assert st == 0, B.ptored_status_string(st)
+        got = dd.download(dtype)
+        wacc = d0.copy()
+        exact, absum = oracle.accumulate_add(fsrcs, wacc, dtype=dtype, rows=rows, cols=cols,
+                                             ld=ld, valid_rows=vr, valid_cols=vc)
+        m = valid_mask(rows, ld, vr, vc, size)
+        assert np.array_equal(got[~m].view(np.uint8), d0[~m].view(np.uint8)), case
+        if dtype == "i32":
+            assert compare(dtype, got[m], wacc[m]).all(), case
+        else:
+            g = oracle.to_double(dtype, bits(dtype, got[m]).astype(np.uint32))
+            bound = n * UNIT[dtype] * absum * 1.0001 + n * TINY[dtype]
+            assert np.all(np.abs(g - exact) <= bound), case
+
+
 def test_allreduce_two_entries_same_buffer():
     """The same buffer listed twice counts as two ranks and gets the result."""
     rng = np.random.default_rng(35)

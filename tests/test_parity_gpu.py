@@ -122,6 +122,65 @@ def test_random_small_cases(dtype):
         _check(srcs, dtype, op, root, rows, cols, ld, vr, vc, dst, bufs, label=label)
 
 
+# Shapes for buffers that all start `lead` bytes past a 16-byte boundary
+# (pitches are multiples of 16 bytes for every element size).
+LEAD_SHAPES = [
+    # rows, cols, ld, valid_rows, valid_cols
+    (1, 5003, 5003, 1, 5003),      # one contiguous span
+    (40, 256, 256, 40, 256),       # rows back to back: contiguous
+    (33, 1030, 1040, 31, 1029),    # 2-D, ragged row ends
+    (9, 4100, 4104, 9, 4099),      # row tiles: 4+ chunks per row
+    (5, 9, 16, 5, 8),              # rows of one head, at most one slot and a tail
+    (1, 7, 7, 1, 7),               # tiny: vector only when lead + 7 elements reach 16 bytes
+    (1, 1, 1, 1, 1),               # one element: never reaches the boundary (element-wise)
+]
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_common_lead_keeps_vector_path(dtype):
+    """Every buffer the same number of bytes past a 16-byte boundary: the
+    vector kernels with a head per row, against the oracle, in every walk,
+    with windows, the runtime rank loop, the LDS variant and in place."""
+    rng = np.random.default_rng({"f32": 71, "bf16": 72, "f16": 73, "i32": 74}[dtype])
+    es = ESIZE[dtype]
+    leads = list(range(es, 16, es))
+    variants = [("auto", 0, 0), ("flat", B.PTORED_FORCE_ROWS | B.PTORED_FLAT_WALK, 0),
+                ("row_tiles", B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES, 0),
+                ("runtime_n", B.PTORED_FORCE_RUNTIME_N, 0), ("lds", B.PTORED_LDS_PINGPONG, 0),
+                ("windows", 0, 1008), ("windows_rows", B.PTORED_FORCE_ROWS, 4096 + 48)]
+    case = 0
+    for rows, cols, ld, vr, vc in LEAD_SHAPES:
+        for vi, (vname, flags, mlb) in enumerate(variants):
+            lead = leads[(case * 3 + vi) % len(leads)]
+            n = int(rng.choice([2, 3, 8, 16, 20]))
+            root = int(rng.integers(0, n))
+            op = OPS[case % 4]
+            offs = [lead + 16 * int(rng.integers(0, 4)) for _ in range(n)]
+            dst_off = lead + 16 * int(rng.integers(0, 4))
+            alias = int(rng.integers(0, n)) if case % 5 == 4 else -1
+            size = (rows - 1) * ld + cols
+            srcs = [_rand_elems(dtype, rng, size) for _ in range(n)]
+            t = B.tuning(flags=flags, max_launch_bytes=mlb)
+            label = f"lead#{case} lead={lead} {vname} {rows}x{cols} ld={ld} valid={vr}x{vc}"
+            st_plan, info = B.ptored_treduce_plan(
+                [0x1000000 + o for o in offs], n, root,
+                0x9000000 + (offs[alias] if alias >= 0 else dst_off), rows, cols, ld, vr, vc,
+                B.DTYPES[dtype], B.OPS[op], t)
+            assert st_plan == 0
+            contig = (vc == ld or vr == 1) and not flags & B.PTORED_FORCE_ROWS
+            row_bytes = ((vc if vr == 1 else vr * ld) if contig else vc) * es
+            # else the element-wise kernel: a row that never reaches the
+            # boundary, or 2-D rows whose pitch is off the 16-byte grid
+            vector = lead + row_bytes >= 16 and (contig or (ld * es) % 16 == 0)
+            assert (B.PATHS[info.path] != "elementwise") == vector, label
+            dst, st, bufs = run_gpu(srcs, dtype, op, root, rows, cols, ld, vr, vc, offsets=offs,
+                                    dst_offset=dst_off, tuning=t, alias=alias, label=label)
+            assert st == 0, B.ptored_status_string(st)
+            _check(srcs, dtype, op, root, rows, cols, ld, vr, vc, dst, bufs, alias=alias,
+                   label=label)
+            case += 1
+
+
 MEDIUM = [
     # rows, cols, ld, valid_rows, valid_cols
     (129, 1000, 1024, 129, 999),
