@@ -379,6 +379,32 @@ def test_accumulate_add_random(dtype):
             assert np.all(np.abs(g - exact) <= bound), case
 
 
+@pytest.mark.parametrize("dtype", DT)
+def test_accumulate_in_one_call_via_treduce(dtype):
+    """dst += src_0 + ... + src_{N-1} in rank order, in one reduction call: dst
+    as the root source and the destination (exact alias).  Bit-exact against
+    the oracle's rank-order accumulation."""
+    rng = np.random.default_rng({"f32": 81, "bf16": 82, "f16": 83, "i32": 84}[dtype])
+    for case in range(6):
+        n = int(rng.choice([1, 3, 8, 15]))
+        rows, cols = int(rng.integers(1, 40)), int(rng.integers(1, 600))
+        ld = cols + int(rng.choice([0, 5, 8]))
+        vr, vc = int(rng.integers(1, rows + 1)), int(rng.integers(1, cols + 1))
+        size = (rows - 1) * ld + cols
+        srcs = [_rand_elems(dtype, rng, size, wild=0.05) for _ in range(n)]
+        d0 = _rand_elems(dtype, rng, size, wild=0.05)
+        bufs = _upload([d0] + srcs, [0] * (n + 1))
+        say(f"accumulate via treduce#{case} {dtype} N={n} {rows}x{cols} ld={ld} valid={vr}x{vc}")
+        st = B.ptored_treduce([b.ptr for b in bufs], n + 1, 0, bufs[0].ptr, rows, cols, ld, vr,
+                              vc, B.DTYPES[dtype], B.OPS["sum"], _stream())
+        torch.cuda.synchronize()
+        assert st == 0, B.ptored_status_string(st)
+        want = d0.copy()
+        oracle.accumulate_add(srcs, want, dtype=dtype, rows=rows, cols=cols, ld=ld,
+                              valid_rows=vr, valid_cols=vc)
+        assert compare(dtype, bufs[0].download(dtype), want).all(), case
+
+
 def test_accumulate_add_full_size_i32_exact():
     w = W.WORKLOADS["n16_i32_4096x4096"]
     srcs = W.make_sources(w)
