@@ -152,7 +152,7 @@ def test_common_lead_keeps_vector_path(dtype):
     for rows, cols, ld, vr, vc in LEAD_SHAPES:
         for vi, (vname, flags, mlb) in enumerate(variants):
             lead = leads[(case * 3 + vi) % len(leads)]
-            n = int(rng.choice([2, 3, 8, 16, 20]))
+            n = int(rng.choice([1, 2, 3, 8, 16, 20]))
             root = int(rng.integers(0, n))
             op = OPS[case % 4]
             offs = [lead + 16 * int(rng.integers(0, 4)) for _ in range(n)]
