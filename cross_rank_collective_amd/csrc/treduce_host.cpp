@@ -500,8 +500,9 @@ int launch_ring(const Plan& p, const RingArgs& a, int cu, hipStream_t s) {
 }
 
 // The ring reduce-scatter in one launch per window of max_launch_bytes (one
-// launch in all for streams up to 2 GiB).  Every stream is 16-byte aligned,
-// so window offsets that are multiples of 16 keep whole slots whole.
+// launch in all for streams up to 2 GiB).  Every stream starts at the same
+// offset within a 16-byte block, so windows counted from that block's start
+// in multiples of 16 keep whole slots whole.
 // `bounds` are the segment boundaries in elements.
 int run_ring(const Plan& plan, const void* const* srcs, void* const* dsts, const int64_t* bounds,
              int64_t count, hipStream_t stream) {
@@ -512,7 +513,9 @@ int run_ring(const Plan& plan, const void* const* srcs, void* const* dsts, const
     const int cu = f.cu;
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     const int n = p.nranks;
-    const int64_t es = p.esize, total = count * es;
+    // Streams that all start `lead` bytes past a 16-byte boundary are
+    // addressed from that boundary; segment bounds move by the same bytes.
+    const int64_t es = p.esize, lead = p.lead, total = lead + count * es;
     RingArgs a{};
     a.nranks = (uint32_t)n;
     a.xcd_remap = p.xcd_remap ? 1u : 0u;
@@ -521,13 +524,13 @@ int run_ring(const Plan& plan, const void* const* srcs, void* const* dsts, const
         const int64_t w1 = std::min(total, w0 + p.max_launch_bytes);
         int s0 = -1, s1 = -1;  // segments that meet [w0, w1)
         for (int s = 0; s < n; ++s)
-            if (bounds[s] * es < w1 && bounds[s + 1] * es > w0) {
+            if (lead + bounds[s] * es < w1 && lead + bounds[s + 1] * es > w0) {
                 if (s0 < 0) s0 = s;
                 s1 = s;
             }
         if (s0 < 0) continue;
         for (int s = 0; s <= n; ++s)
-            a.bounds[s] = (uint32_t)std::clamp<int64_t>(bounds[s] * es - w0, 0, w1 - w0);
+            a.bounds[s] = (uint32_t)std::clamp<int64_t>(lead + bounds[s] * es - w0, 0, w1 - w0);
         uint32_t main_max = 0, edge = 0;
         for (int s = s0; s <= s1; ++s) {
             const uint32_t lo = a.bounds[s], hi = a.bounds[s + 1];
@@ -540,8 +543,8 @@ int run_ring(const Plan& plan, const void* const* srcs, void* const* dsts, const
         }
         if (main_max + edge == 0) continue;
         for (int r = 0; r < n; ++r) {
-            a.src[r] = a.src[r + n] = static_cast<const char*>(srcs[r]) + w0;
-            a.dst[r] = static_cast<char*>(dsts[r]) + w0;
+            a.src[r] = a.src[r + n] = static_cast<const char*>(srcs[r]) - lead + w0;
+            a.dst[r] = static_cast<char*>(dsts[r]) - lead + w0;
         }
         a.extent = (uint32_t)(w1 - w0);
         a.seg0 = (uint32_t)s0;
@@ -669,8 +672,7 @@ extern "C" int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, v
         st = make_plan(ptrs, 2 * nranks, nranks, 1, count, count, dtype, op, tuning, kModeReduce,
                        p);
         if (st != PTORED_OK) return st;
-        if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages &&
-            p.lead == 0) {
+        if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages) {
             if (p.wgs_per_cu > 0)  // the ring kernel moves one slot per thread
                 p.wgs_per_cu = wgs_per_cu_for((uint64_t)(nranks + 1) * kBlock * 16u);
             return run_ring(p, srcs, dsts, bounds, count, stream);

@@ -215,8 +215,8 @@ int ptored_ring_bounds(int64_t count, int nranks, int dtype, int64_t* bounds);
  *             elements.  dsts[s] may be srcs[s] (in place into the owner's
  *             window), any other source or another dst; partial overlaps are
  *             rejected.
- * Errors as ptored_treduce_ex.  When every source and dst is 16-byte
- * aligned, one launch covers every segment (a window of at most
+ * Errors as ptored_treduce_ex.  When every source and dst starts at the same
+ * offset within a 16-byte block, one launch covers every segment (a window of at most
  * max_launch_bytes per launch): each workgroup takes one segment's tile and
  * folds it in that segment's ring order, and one more tile per segment
  * folds its elements outside whole 16-byte slots.  Otherwise, or with
