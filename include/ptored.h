@@ -26,7 +26,8 @@
  * the end, so an integer keeps its meaning ([N6] "ABI enums").
  *
  * All functions are thread-safe.  No function allocates device memory; the
- * library keeps no state besides a per-device cache of the compute-unit count.
+ * library keeps no state besides a per-device cache of the compute-unit count
+ * and LDS sizes.
  */
 #ifndef PTORED_H
 #define PTORED_H

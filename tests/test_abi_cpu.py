@@ -265,3 +265,26 @@ def test_collective_argument_errors_before_any_hip_call():
     # accumulate: dst may not alias a source, even exactly
     assert lib.ptored_accumulate_add(A[:2], 2, A[1], 4, 4, 4, 4, 4, 0, None, s) == -3
     assert lib.ptored_accumulate_add(A[:2], 2, D, 4, 4, 4, 0, 4, 0, None, s) == 0  # empty
+
+
+def test_header_as_c11_against_the_library(tmp_path):
+    """include/ptored.h compiled as C11 (gcc, warnings as errors) and linked
+    with the built library: layouts, enum values, plans, argument errors and
+    ring bounds checked from C (tests/c_abi_check.c); no HIP call is made."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    libdir = os.path.join(root, "cross_rank_collective_amd")
+    exe = str(tmp_path / "c_abi_check")
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I" + os.path.join(root, "include"), "-I/opt/rocm/include",
+           os.path.join(here, "c_abi_check.c"), "-L" + libdir, "-lptored",
+           "-Wl,-rpath," + libdir, "-o", exe]
+    subprocess.run(cmd, check=True)
+    out = subprocess.run([exe], capture_output=True, text=True)
+    assert out.returncode == 0 and "c abi ok" in out.stdout, out.stdout + out.stderr
