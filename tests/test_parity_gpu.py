@@ -313,6 +313,28 @@ def test_empty_region_launches_nothing_and_writes_nothing():
         assert np.all(d.download_all() == 0xFF)
 
 
+@pytest.mark.parametrize("dtype", DT)
+def test_single_rank_is_a_bitwise_copy(dtype):
+    """N == 1 copies the bits unchanged ([TREDUCE] §4.3 single-rank case):
+    every 16-bit pattern (NaN payloads and signaling NaNs included) for the
+    16-bit types, random 32-bit patterns plus signaling NaNs for f32 and i32;
+    compared bit for bit, not by NaN-ness."""
+    if ESIZE[dtype] == 2:
+        src = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    else:
+        rng = np.random.default_rng(5)
+        src = rng.integers(0, 2 ** 32, 1 << 16, dtype=np.uint64).astype(np.uint32)
+        src[:4] = [0x7F800001, 0xFF800001, 0x7FBFFFFF, 0x7FC00001]  # sNaNs, payload qNaN
+    src = src.view(STORAGE[dtype])
+    n = src.size
+    for flags in (0, B.PTORED_FORCE_ELEMENTWISE):
+        dst, st, bufs = run_gpu([src], dtype, "sum", 0, 1, n, n, 1, n,
+                                tuning=B.tuning(flags=flags), label=f"copy flags={flags}")
+        assert st == 0, B.ptored_status_string(st)
+        got = dst.download(dtype)
+        assert np.array_equal(got.view(np.uint8), src.view(np.uint8)), flags
+
+
 def test_tensor_wrapper_and_side_stream():
     torch.manual_seed(0)
     xs = [torch.randn(300, 500, device="cuda") for _ in range(5)]
