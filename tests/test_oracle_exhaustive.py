@@ -8,8 +8,9 @@ the element type.  The two agree only if the oracle's own rounding is right
 for every sum and product of two 16-bit values, and if rounding through
 binary32 first is innocuous for these formats (Figueroa, "When is double
 rounding innocuous?", SIGNUM Newsletter 30(3), 1995: 24 >= 2p + 2 for p = 11
-and p = 8), the reading the GPU kernels rely on.  NaN results are compared
-by NaN-ness only.
+and p = 8), the reading the GPU kernels rely on.  Max and Min are checked
+against the extremum by an integer order key of the bit patterns (-0 below
++0; any NaN operand gives a NaN).  NaN results are compared by NaN-ness only.
 
 About a CPU-minute per case on 8 cores: skipped unless PTORED_EXHAUSTIVE=1.
 """
@@ -33,6 +34,13 @@ def _isnan(dtype, bits):
     return ((bits >> 7) & 0xFF == 0xFF) & (bits & 0x7F != 0)
 
 
+def _order_key(bits):
+    """Integer key of a 16-bit float pattern in value order, -0 below +0
+    (sign-magnitude to a monotone unsigned key); meaningless for NaNs."""
+    neg = (bits & 0x8000) != 0
+    return np.where(neg, 0x7FFF - (bits & 0x7FFF), 0x8000 + (bits & 0x7FFF))
+
+
 def _task(args):
     """Mismatches for a in [a0, a0 + ROWS_PER_TASK) and every b."""
     dtype, op, a0 = args
@@ -44,6 +52,18 @@ def _task(args):
     a = np.repeat(np.arange(a0, a0 + ROWS_PER_TASK, dtype=np.uint32), 65536)
     bb = np.tile(b, ROWS_PER_TASK)
     got = oracle.combine_bits(dtype, op, a, bb).astype(np.uint32)
+    if op in ("max", "min"):
+        # the extremum by the order key; any NaN operand gives a NaN
+        ka, kb = _order_key(a), _order_key(bb)
+        pick_b = kb > ka if op == "max" else kb < ka
+        want = np.where(pick_b, bb, a).astype(np.uint32)
+        nan_in = _isnan(dtype, a) | _isnan(dtype, bb)
+        want = np.where(nan_in, 0x7FFF if dtype == "bf16" else 0x7E00, want).astype(np.uint32)
+        ng, nw = _isnan(dtype, got), _isnan(dtype, want)
+        bad = np.where(ng | nw, ng != nw, got != want)
+        idx = np.nonzero(bad)[0]
+        return int(idx.size), [(int(a[i]), int(bb[i]), int(got[i]), int(want[i]))
+                               for i in idx[:5]]
     tdt = torch.float16 if dtype == "f16" else torch.bfloat16
     ta = torch.from_numpy(a.astype(np.uint16).view(np.int16)).view(tdt).float()
     tb = torch.from_numpy(bb.astype(np.uint16).view(np.int16)).view(tdt).float()
@@ -56,7 +76,8 @@ def _task(args):
 
 
 @pytest.mark.parametrize("dtype,op", [("f16", "sum"), ("f16", "prod"), ("bf16", "sum"),
-                                      ("bf16", "prod")])
+                                      ("bf16", "prod"), ("f16", "max"), ("f16", "min"),
+                                      ("bf16", "max"), ("bf16", "min")])
 def test_all_pairs_match_binary32_then_round(dtype, op):
     tasks = [(dtype, op, a0) for a0 in range(0, 65536, ROWS_PER_TASK)]
     workers = max(1, min(8, os.cpu_count() or 1))
