@@ -9,6 +9,8 @@ from .binding import (  # noqa: F401
     DTYPES,
     OPS,
     PtoredError,
+    accumulate_add,
+    allreduce,
     load,
     ptored_abi_version,
     ptored_accumulate_add,
@@ -20,6 +22,8 @@ from .binding import (  # noqa: F401
     ptored_treduce,
     ptored_treduce_ex,
     ptored_treduce_plan,
+    reduce_scatter_ring,
+    ring_bounds,
     treduce,
     tuning,
 )

@@ -180,13 +180,22 @@ def tuning(flags: int = 0, blocks_per_cu: int = 0, max_launch_bytes: int = 0) ->
     return ptored_tuning(flags, blocks_per_cu, max_launch_bytes)
 
 
-def _torch_dtype_code(t) -> int:
+def _dtype_code(dtype) -> int:
+    """C ABI code of a torch dtype or of one of "f32", "bf16", "f16", "i32"."""
+    if isinstance(dtype, str):
+        if dtype not in DTYPES:
+            raise TypeError(f"unsupported dtype {dtype!r}; expected f32, bf16, f16 or i32")
+        return DTYPES[dtype]
     import torch
 
     codes = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2, torch.int32: 3}
-    if t.dtype not in codes:
-        raise TypeError(f"unsupported dtype {t.dtype}; expected f32, bf16, f16 or i32")
-    return codes[t.dtype]
+    if dtype not in codes:
+        raise TypeError(f"unsupported dtype {dtype}; expected f32, bf16, f16 or i32")
+    return codes[dtype]
+
+
+def _torch_dtype_code(t) -> int:
+    return _dtype_code(t.dtype)
 
 
 def _geometry(t) -> Tuple[int, int, int]:
@@ -195,6 +204,30 @@ def _geometry(t) -> Tuple[int, int, int]:
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError("tensors must be 1-D or 2-D row-major with unit column stride")
     return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _check_group(tensors, ref, what: str):
+    """Every tensor matches `ref` in dtype, geometry and device."""
+    geo = _geometry(ref)
+    for t in tensors:
+        if t.dtype != ref.dtype or _geometry(t) != geo:
+            raise ValueError(f"every {what} must match in dtype and geometry")
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError(f"every {what} must be on the same GPU")
+    return geo
+
+
+def _stream_handle(stream, device) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _raise_on(st: int) -> None:
+    if st != PTORED_OK:
+        raise PtoredError(st, ptored_status_string(st))
 
 
 def treduce(srcs, dst, op: str = "sum", root: int = 0,
@@ -212,19 +245,79 @@ def treduce(srcs, dst, op: str = "sum", root: int = 0,
     if len(srcs) == 0:
         raise ValueError("treduce needs at least one source")
     dt = _torch_dtype_code(dst)
-    geo = _geometry(dst)
-    for s in srcs:
-        if s.dtype != dst.dtype or _geometry(s) != geo:
-            raise ValueError("every source must match dst in dtype and geometry")
-        if not s.is_cuda or s.device != dst.device:
-            raise ValueError("every tensor must be on dst's GPU")
-    rows, cols, ld = geo
+    rows, cols, ld = _check_group(list(srcs) + [dst], dst, "tensor")
     vr, vc = (rows, cols) if valid is None else valid
-    if stream is None:
-        stream = torch.cuda.current_stream(dst.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, dst.device)
     with torch.cuda.device(dst.device):
-        st = ptored_treduce_ex([s.data_ptr() for s in srcs], len(srcs), root, dst.data_ptr(),
-                               rows, cols, ld, vr, vc, dt, OPS[op], tuning, handle)
-    if st != PTORED_OK:
-        raise PtoredError(st, ptored_status_string(st))
+        _raise_on(ptored_treduce_ex([s.data_ptr() for s in srcs], len(srcs), root,
+                                    dst.data_ptr(), rows, cols, ld, vr, vc, dt, OPS[op], tuning,
+                                    handle))
+
+
+def allreduce(bufs, op: str = "sum", root: int = 0, valid: Optional[Tuple[int, int]] = None,
+              tuning: Optional[ptored_tuning] = None, stream=None) -> None:
+    """In place: every tensor's valid rectangle becomes the fold of all of them
+    (root first, then ascending).  Geometry and stream as ``treduce``."""
+    import torch
+
+    if len(bufs) == 0:
+        raise ValueError("allreduce needs at least one buffer")
+    dt = _torch_dtype_code(bufs[0])
+    rows, cols, ld = _check_group(bufs, bufs[0], "buffer")
+    vr, vc = (rows, cols) if valid is None else valid
+    handle = _stream_handle(stream, bufs[0].device)
+    with torch.cuda.device(bufs[0].device):
+        _raise_on(ptored_allreduce([b.data_ptr() for b in bufs], len(bufs), root, rows, cols,
+                                   ld, vr, vc, dt, OPS[op], tuning, handle))
+
+
+def ring_bounds(count: int, nranks: int, dtype) -> list:
+    """The ring schedule's segment boundaries: nranks + 1 element offsets.
+    ``dtype`` is a torch dtype or one of "f32", "bf16", "f16", "i32"."""
+    st, out = ptored_ring_bounds(count, nranks, _dtype_code(dtype))
+    _raise_on(st)
+    return out
+
+
+def reduce_scatter_ring(srcs, dsts, op: str = "sum", tuning: Optional[ptored_tuning] = None,
+                        stream=None) -> None:
+    """The ring reduce-scatter share on one GPU: the N contiguous source
+    streams (all elements of each tensor) are cut into the ring's segments,
+    and segment s, folded in ring order (ranks s+1, ..., s mod N), is written
+    to dsts[s] at the same positions; nothing else of any dst is written."""
+    import torch
+
+    if len(srcs) == 0 or len(dsts) != len(srcs):
+        raise ValueError("reduce_scatter_ring needs one dst per source")
+    ref = srcs[0]
+    for t in list(srcs) + list(dsts):
+        if not t.is_contiguous():
+            raise ValueError("reduce_scatter_ring streams must be contiguous")
+        if t.dtype != ref.dtype or t.numel() != ref.numel():
+            raise ValueError("every stream must match in dtype and length")
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError("every stream must be on the same GPU")
+    dt = _torch_dtype_code(ref)
+    handle = _stream_handle(stream, ref.device)
+    with torch.cuda.device(ref.device):
+        _raise_on(ptored_reduce_scatter_ring([s.data_ptr() for s in srcs], len(srcs),
+                                             [d.data_ptr() for d in dsts], ref.numel(), dt,
+                                             OPS[op], tuning, handle))
+
+
+def accumulate_add(srcs, dst, valid: Optional[Tuple[int, int]] = None,
+                   tuning: Optional[ptored_tuning] = None, stream=None) -> None:
+    """Push-with-add: dst += every source over the valid rectangle, by
+    device-scope atomics (the additions land in an unspecified order).
+    Geometry and stream as ``treduce``; dst may not be a source."""
+    import torch
+
+    if len(srcs) == 0:
+        raise ValueError("accumulate_add needs at least one source")
+    dt = _torch_dtype_code(dst)
+    rows, cols, ld = _check_group(list(srcs) + [dst], dst, "tensor")
+    vr, vc = (rows, cols) if valid is None else valid
+    handle = _stream_handle(stream, dst.device)
+    with torch.cuda.device(dst.device):
+        _raise_on(ptored_accumulate_add([s.data_ptr() for s in srcs], len(srcs), dst.data_ptr(),
+                                        rows, cols, ld, vr, vc, dt, tuning, handle))

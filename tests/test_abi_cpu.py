@@ -288,3 +288,23 @@ def test_header_as_c11_against_the_library(tmp_path):
     subprocess.run(cmd, check=True)
     out = subprocess.run([exe], capture_output=True, text=True)
     assert out.returncode == 0 and "c abi ok" in out.stdout, out.stdout + out.stderr
+
+
+def test_tensor_wrappers_reject_bad_groups():
+    """The tensor wrappers check their arguments before calling the library."""
+    import torch
+
+    import cross_rank_collective_amd as crc
+
+    a = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        crc.allreduce([])
+    with pytest.raises(ValueError):
+        crc.reduce_scatter_ring([a], [])
+    with pytest.raises(ValueError):
+        crc.accumulate_add([], a)
+    with pytest.raises(TypeError):
+        crc.ring_bounds(10, 2, torch.float64)
+    with pytest.raises(ValueError):  # CPU tensors are not on a GPU
+        crc.allreduce([a, torch.zeros(4, 8)])
+    assert crc.ring_bounds(100, 4, "bf16") == [0, 32, 64, 80, 100]

@@ -419,3 +419,52 @@ def test_accumulate_add_full_size_i32_exact():
     want = d0.astype(np.int64) + np.sum(np.stack([s.astype(np.int64) for s in srcs]), axis=0)
     want = ((want + 2**31) % 2**32 - 2**31).astype(np.int32)
     assert np.array_equal(db.download("i32"), want)
+
+
+# ------------------------------------------------------------ tensor wrappers ---
+
+def test_tensor_wrappers_of_the_collectives():
+    """allreduce / reduce_scatter_ring / accumulate_add / ring_bounds on torch
+    tensors (2-D views with a pitch, a side stream) against the oracle."""
+    import cross_rank_collective_amd as crc
+
+    rng = np.random.default_rng(97)
+    n, rows, cols, ld = 5, 37, 300, 304
+    host = [rng.standard_normal((rows, ld)).astype(np.float32) for _ in range(n)]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        bufs = [torch.from_numpy(h).cuda()[:, :cols] for h in host]   # 2-D views, ld 304
+        crc.allreduce(bufs, op="max", root=2, valid=(rows - 1, cols - 3))
+    s.synchronize()
+    want = [h.reshape(-1).copy() for h in host]
+    oracle.allreduce_inplace(want, root=2, dtype="f32", op="max", rows=rows, cols=ld, ld=ld,
+                             valid_rows=rows - 1, valid_cols=cols - 3)
+    for b, w_ in zip(bufs, want):
+        got = b.cpu().numpy()
+        assert np.array_equal(got, w_.reshape(rows, ld)[:, :cols])
+
+    count = 10007
+    srcs = [torch.from_numpy(rng.integers(-2 ** 20, 2 ** 20, count, dtype=np.int32)).cuda()
+            for _ in range(n)]
+    dsts = [torch.full((count,), -1, dtype=torch.int32, device="cuda") for _ in range(n)]
+    crc.reduce_scatter_ring(srcs, dsts, op="sum")
+    torch.cuda.synchronize()
+    want = [sentinel("i32", count) for _ in range(n)]
+    oracle.reduce_scatter_ring([t.cpu().numpy() for t in srcs], want, count=count, dtype="i32",
+                               op="sum")
+    for d, w_ in zip(dsts, want):
+        assert np.array_equal(d.cpu().numpy(), w_)
+    assert crc.ring_bounds(count, n, torch.int32) == list(oracle.ring_bounds(count, n, "i32"))
+
+    srcs = [torch.from_numpy(rng.integers(-2 ** 20, 2 ** 20, (rows, cols), dtype=np.int32))
+            .cuda() for _ in range(n)]
+    d0 = rng.integers(-2 ** 20, 2 ** 20, (rows, cols), dtype=np.int32)
+    dst = torch.from_numpy(d0).cuda()
+    crc.accumulate_add(srcs, dst, valid=(rows, cols - 1))
+    torch.cuda.synchronize()
+    want = d0.reshape(-1).copy()
+    oracle.accumulate_add([t.cpu().numpy().reshape(-1) for t in srcs], want, dtype="i32",
+                          rows=rows, cols=cols, ld=cols, valid_rows=rows, valid_cols=cols - 1)
+    assert np.array_equal(dst.cpu().numpy().reshape(-1), want)
+    with pytest.raises(crc.PtoredError):
+        crc.accumulate_add(srcs, srcs[0])  # dst may not be a source
