@@ -422,7 +422,6 @@ int run(const Plan& plan, const char* const* ordered, void* dst, hipStream_t str
     if (st != PTORED_OK) return st;
     const Plan p = with_device(plan, f);
     const int cu = f.cu;
-    (void)hipGetLastError();  // clear a stale error so the check below is ours
 
     KArgs a{};
     a.nranks = (uint32_t)p.nranks;
@@ -449,9 +448,8 @@ int run(const Plan& plan, const char* const* ordered, void* dst, hipStream_t str
         for (int64_t r = 0; r < p.valid_rows && rc == 0; ++r)
             rc = launch_run(p, a, base, d, r * p.ld * es, p.lead, row_end, cu, stream);
     }
-    if (rc != 0) return PTORED_ERR_UNSUPPORTED;
-    if (hipGetLastError() != hipSuccess) return PTORED_ERR_HIP;
-    return PTORED_OK;
+    if (rc == kLaunchNoKernel) return PTORED_ERR_UNSUPPORTED;
+    return rc == kLaunchOk ? PTORED_OK : PTORED_ERR_HIP;
 }
 
 // TREDUCE arguments: validate, then plan.  ptrs = sources then dst.
@@ -511,7 +509,6 @@ int run_ring(const Plan& plan, const void* const* srcs, void* const* dsts, const
     if (st != PTORED_OK) return st;
     const Plan p = with_device(plan, f);
     const int cu = f.cu;
-    (void)hipGetLastError();  // clear a stale error so the check below is ours
     const int n = p.nranks;
     // Streams that all start `lead` bytes past a 16-byte boundary are
     // addressed from that boundary; segment bounds move by the same bytes.
@@ -554,9 +551,8 @@ int run_ring(const Plan& plan, const void* const* srcs, void* const* dsts, const
         a.div_seg = fast_div_for(a.tiles_per_seg);
         rc = launch_ring(p, a, cu, stream);
     }
-    if (rc != 0) return PTORED_ERR_UNSUPPORTED;
-    if (hipGetLastError() != hipSuccess) return PTORED_ERR_HIP;
-    return PTORED_OK;
+    if (rc == kLaunchNoKernel) return PTORED_ERR_UNSUPPORTED;
+    return rc == kLaunchOk ? PTORED_OK : PTORED_ERR_HIP;
 }
 
 }  // namespace

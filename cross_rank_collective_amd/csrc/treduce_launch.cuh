@@ -22,8 +22,8 @@ namespace ptored {
 // many blocks per CU; blocks_per_cu < 0: a persistent grid at the kernel's
 // occupancy.
 template <auto KERNEL, class ARGS>
-static void launch_grid(const Plan& p, const ARGS& a, uint64_t tiles, int cu_count,
-                        hipStream_t s) {
+static int launch_grid(const Plan& p, const ARGS& a, uint64_t tiles, int cu_count,
+                       hipStream_t s) {
     uint64_t grid = tiles;
     if (p.blocks_per_cu != 0) {
         int per_cu = p.blocks_per_cu;
@@ -55,37 +55,38 @@ static void launch_grid(const Plan& p, const ARGS& a, uint64_t tiles, int cu_cou
         if (static_lds >= 0 && (int64_t)p.cap_lds > static_lds)
             shmem = p.cap_lds - (uint32_t)static_lds;
     }
-    hipLaunchKernelGGL(KERNEL, dim3((uint32_t)grid), dim3(kBlock), shmem, s, a);
+    // the launch's own status: the caller's last-error state is left alone
+    void* args[] = {const_cast<ARGS*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(KERNEL), dim3((uint32_t)grid),
+                           dim3(kBlock), args, shmem, s) == hipSuccess
+               ? kLaunchOk
+               : kLaunchFailed;
 }
 
 template <auto KERNEL>
-static void launch(const Plan& p, const KArgs& a, int cu_count, hipStream_t s) {
-    launch_grid<KERNEL>(p, a, a.total_tiles, cu_count, s);
+static int launch(const Plan& p, const KArgs& a, int cu_count, hipStream_t s) {
+    return launch_grid<KERNEL>(p, a, a.total_tiles, cu_count, s);
 }
 
 template <int DT, int OP, int ES, int WALK, bool ALL>
 static int dispatch_n(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
     if (p.family == kFamElem) {
         if constexpr (WALK == kWalkRowTiles) {
-            return -1;  // the element-wise path never takes row tiles
+            return kLaunchNoKernel;  // the element-wise path never takes row tiles
         } else {
-            launch<treduce_kernel<DT, OP, ES, 0, 1, WALK, false, ALL>>(p, a, cu, s);
-            return 0;
+            return launch<treduce_kernel<DT, OP, ES, 0, 1, WALK, false, ALL>>(p, a, cu, s);
         }
     }
     switch (p.family == kFamVecFixed ? p.nranks : 0) {
-#define PTORED_CASE(n)                                                                 \
-    case n:                                                                            \
-        launch<treduce_kernel<DT, OP, ES, n, unroll_for(n), WALK, true, ALL>>(p, a, cu, s); \
-        return 0;
+#define PTORED_CASE(n) \
+    case n: return launch<treduce_kernel<DT, OP, ES, n, unroll_for(n), WALK, true, ALL>>(p, a, cu, s);
         PTORED_CASE(2) PTORED_CASE(3) PTORED_CASE(4) PTORED_CASE(5) PTORED_CASE(6)
         PTORED_CASE(7) PTORED_CASE(8) PTORED_CASE(9) PTORED_CASE(10) PTORED_CASE(11)
         PTORED_CASE(12) PTORED_CASE(13) PTORED_CASE(14) PTORED_CASE(15) PTORED_CASE(16)
 #undef PTORED_CASE
     case 0:
-        launch<treduce_kernel<DT, OP, ES, 0, kRuntimeUnroll, WALK, true, ALL>>(p, a, cu, s);
-        return 0;
-    default: return -1;
+        return launch<treduce_kernel<DT, OP, ES, 0, kRuntimeUnroll, WALK, true, ALL>>(p, a, cu, s);
+    default: return kLaunchNoKernel;
     }
 }
 
@@ -96,18 +97,16 @@ static int dispatch_op(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
         case kWalkContig: return dispatch_n<DT, OP, ES, kWalkContig, true>(p, a, cu, s);
         case kWalkRowTiles: return dispatch_n<DT, OP, ES, kWalkRowTiles, true>(p, a, cu, s);
         case kWalkFlat: return dispatch_n<DT, OP, ES, kWalkFlat, true>(p, a, cu, s);
-        default: return -1;
+        default: return kLaunchNoKernel;
         }
     }
     if (p.lds_stages) {  // LDS ping-pong variant: contiguous or flattened walks
         switch (p.rows_mode) {
         case kWalkContig:
-            launch<treduce_lds_kernel<DT, OP, ES, kWalkContig, kLdsStages>>(p, a, cu, s);
-            return 0;
+            return launch<treduce_lds_kernel<DT, OP, ES, kWalkContig, kLdsStages>>(p, a, cu, s);
         case kWalkFlat:
-            launch<treduce_lds_kernel<DT, OP, ES, kWalkFlat, kLdsStages>>(p, a, cu, s);
-            return 0;
-        default: return -1;
+            return launch<treduce_lds_kernel<DT, OP, ES, kWalkFlat, kLdsStages>>(p, a, cu, s);
+        default: return kLaunchNoKernel;
         }
     }
     switch (p.rows_mode) {
@@ -119,10 +118,13 @@ static int dispatch_op(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
 
 // Push-with-add: a 2-D grid, one row of workgroups per rank.
 template <int DT, int ES, int WALK, bool VEC>
-static void launch_accumulate(const KArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((accumulate_kernel<DT, ES, WALK, VEC>),
-                       dim3(a.total_tiles > 0 ? a.total_tiles : 1, a.nranks), dim3(kBlock), 0, s,
-                       a);
+static int launch_accumulate(const KArgs& a, hipStream_t s) {
+    void* args[] = {const_cast<KArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(accumulate_kernel<DT, ES, WALK, VEC>),
+                           dim3(a.total_tiles > 0 ? a.total_tiles : 1, a.nranks), dim3(kBlock),
+                           args, 0, s) == hipSuccess
+               ? kLaunchOk
+               : kLaunchFailed;
 }
 
 template <int DT, int ES>
@@ -130,14 +132,12 @@ static int dispatch_accumulate(const Plan& p, const KArgs& a, hipStream_t s) {
     const bool vec = p.family != kFamElem;
     switch (p.rows_mode) {
     case kWalkContig:
-        if (vec) launch_accumulate<DT, ES, kWalkContig, true>(a, s);
-        else launch_accumulate<DT, ES, kWalkContig, false>(a, s);
-        return 0;
+        return vec ? launch_accumulate<DT, ES, kWalkContig, true>(a, s)
+                   : launch_accumulate<DT, ES, kWalkContig, false>(a, s);
     case kWalkFlat:
-        if (vec) launch_accumulate<DT, ES, kWalkFlat, true>(a, s);
-        else launch_accumulate<DT, ES, kWalkFlat, false>(a, s);
-        return 0;
-    default: return -1;
+        return vec ? launch_accumulate<DT, ES, kWalkFlat, true>(a, s)
+                   : launch_accumulate<DT, ES, kWalkFlat, false>(a, s);
+    default: return kLaunchNoKernel;
     }
 }
 
@@ -148,16 +148,15 @@ static int dispatch_copy(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
     constexpr int U = unroll_for(1);
     switch (p.rows_mode) {
     case kWalkContig:
-        launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkContig, true, false>>(p, a, cu, s);
-        break;
+        return launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkContig, true, false>>(p, a,
+                                                                                        cu, s);
     case kWalkRowTiles:
-        launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkRowTiles, true, false>>(p, a, cu, s);
-        break;
+        return launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkRowTiles, true, false>>(p, a,
+                                                                                          cu, s);
     default:
-        launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkFlat, true, false>>(p, a, cu, s);
-        break;
+        return launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkFlat, true, false>>(p, a, cu,
+                                                                                      s);
     }
-    return 0;
 }
 
 // The single-launch ring reduce-scatter: N unrolled for 2 <= N <= 16.
@@ -165,18 +164,15 @@ template <int DT, int OP, int ES>
 static int dispatch_ring_n(const Plan& p, const RingArgs& a, int cu, hipStream_t s) {
     const uint64_t tiles = (uint64_t)a.nseg * a.tiles_per_seg;
     switch (p.family == kFamVecFixed ? p.nranks : 0) {
-#define PTORED_CASE(n)                                                  \
-    case n:                                                             \
-        launch_grid<ring_kernel<DT, OP, ES, n>>(p, a, tiles, cu, s);    \
-        return 0;
+#define PTORED_CASE(n) \
+    case n: return launch_grid<ring_kernel<DT, OP, ES, n>>(p, a, tiles, cu, s);
         PTORED_CASE(2) PTORED_CASE(3) PTORED_CASE(4) PTORED_CASE(5) PTORED_CASE(6)
         PTORED_CASE(7) PTORED_CASE(8) PTORED_CASE(9) PTORED_CASE(10) PTORED_CASE(11)
         PTORED_CASE(12) PTORED_CASE(13) PTORED_CASE(14) PTORED_CASE(15) PTORED_CASE(16)
 #undef PTORED_CASE
     case 0:
-        launch_grid<ring_kernel<DT, OP, ES, 0>>(p, a, tiles, cu, s);
-        return 0;
-    default: return -1;
+        return launch_grid<ring_kernel<DT, OP, ES, 0>>(p, a, tiles, cu, s);
+    default: return kLaunchNoKernel;
     }
 }
 
@@ -187,7 +183,7 @@ static int dispatch_ring(const Plan& p, const RingArgs& a, int cu, hipStream_t s
     case PTORED_MAX: return dispatch_ring_n<DT, PTORED_MAX, ES>(p, a, cu, s);
     case PTORED_MIN: return dispatch_ring_n<DT, PTORED_MIN, ES>(p, a, cu, s);
     case PTORED_PROD: return dispatch_ring_n<DT, PTORED_PROD, ES>(p, a, cu, s);
-    default: return -1;
+    default: return kLaunchNoKernel;
     }
 }
 
@@ -200,7 +196,7 @@ static int dispatch_dtype(const Plan& p, const KArgs& a, int cu, hipStream_t s) 
     case PTORED_MAX: return dispatch_op<DT, PTORED_MAX, ES>(p, a, cu, s);
     case PTORED_MIN: return dispatch_op<DT, PTORED_MIN, ES>(p, a, cu, s);
     case PTORED_PROD: return dispatch_op<DT, PTORED_PROD, ES>(p, a, cu, s);
-    default: return -1;
+    default: return kLaunchNoKernel;
     }
 }
 

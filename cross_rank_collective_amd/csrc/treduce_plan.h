@@ -116,6 +116,13 @@ struct Plan {
     int64_t launches;
 };
 
+// Result of the per-type launch functions.
+enum LaunchStatus : int {
+    kLaunchOk = 0,         // the kernel was launched
+    kLaunchNoKernel = -1,  // no kernel instance for this plan
+    kLaunchFailed = -2,    // the runtime refused the launch
+};
+
 // Threads per workgroup (four waves).
 constexpr int kBlock = 256;
 
