@@ -1,4 +1,6 @@
-// treduce_bf16.hip -- kernel instances and launcher for bf16 elements.
+// treduce_bf16.hip -- launchers for bf16 elements: the copy and push-with-add
+// kernel instances, and the per-operator selection of the reduction and ring
+// instances (treduce_op.hip).
 #include "treduce_launch.cuh"
 
 namespace ptored {
@@ -8,7 +10,7 @@ int launch_bf16(const Plan& p, const KArgs& a, int cu_count, hipStream_t stream)
 }
 
 int launch_ring_bf16(const Plan& p, const RingArgs& a, int cu_count, hipStream_t stream) {
-    return dispatch_ring<PTORED_BF16, 2>(p, a, cu_count, stream);
+    return dispatch_ring<PTORED_BF16>(p, a, cu_count, stream);
 }
 
 }  // namespace ptored

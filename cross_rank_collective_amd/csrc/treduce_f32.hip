@@ -1,4 +1,6 @@
-// treduce_f32.hip -- kernel instances and launcher for f32 elements.
+// treduce_f32.hip -- launchers for f32 elements: the copy and push-with-add
+// kernel instances, and the per-operator selection of the reduction and ring
+// instances (treduce_op.hip).
 #include "treduce_launch.cuh"
 
 namespace ptored {
@@ -8,7 +10,7 @@ int launch_f32(const Plan& p, const KArgs& a, int cu_count, hipStream_t stream) 
 }
 
 int launch_ring_f32(const Plan& p, const RingArgs& a, int cu_count, hipStream_t stream) {
-    return dispatch_ring<PTORED_F32, 4>(p, a, cu_count, stream);
+    return dispatch_ring<PTORED_F32>(p, a, cu_count, stream);
 }
 
 }  // namespace ptored

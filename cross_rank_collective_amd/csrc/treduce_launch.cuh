@@ -1,10 +1,12 @@
-// treduce_launch.cuh -- kernel selection for one element type.
+// treduce_launch.cuh -- kernel selection.
 //
-// Included once per element type (treduce_<type>.hip) so the four types
-// compile in parallel.  Maps a Plan onto one template instance: the rank
-// count N is a compile-time constant for 1 <= N <= 16 (fully unrolled
-// loads); larger or forced counts and the element-wise path take the
-// runtime rank loop.
+// Maps a Plan onto one template instance: the rank count N is a
+// compile-time constant for 1 <= N <= 16 (fully unrolled loads); larger or
+// forced counts and the element-wise path take the runtime rank loop.  The
+// reduction and ring kernels of each (element type, operator) pair are
+// instantiated in a translation unit of their own (treduce_op.hip, built
+// once per pair) and the copy and push-with-add kernels in one per element
+// type (treduce_<type>.hip), so the units compile in parallel.
 #pragma once
 
 #include "accumulate_kernels.cuh"
@@ -176,13 +178,20 @@ static int dispatch_ring_n(const Plan& p, const RingArgs& a, int cu, hipStream_t
     }
 }
 
-template <int DT, int ES>
+// The reduction and ring launchers of one (element type, operator) pair,
+// defined and explicitly instantiated in treduce_op.hip.
+template <int DT, int OP>
+int launch_op(const Plan& p, const KArgs& a, int cu_count, hipStream_t stream);
+template <int DT, int OP>
+int launch_ring_op(const Plan& p, const RingArgs& a, int cu_count, hipStream_t stream);
+
+template <int DT>
 static int dispatch_ring(const Plan& p, const RingArgs& a, int cu, hipStream_t s) {
     switch (p.op) {
-    case PTORED_SUM: return dispatch_ring_n<DT, PTORED_SUM, ES>(p, a, cu, s);
-    case PTORED_MAX: return dispatch_ring_n<DT, PTORED_MAX, ES>(p, a, cu, s);
-    case PTORED_MIN: return dispatch_ring_n<DT, PTORED_MIN, ES>(p, a, cu, s);
-    case PTORED_PROD: return dispatch_ring_n<DT, PTORED_PROD, ES>(p, a, cu, s);
+    case PTORED_SUM: return launch_ring_op<DT, PTORED_SUM>(p, a, cu, s);
+    case PTORED_MAX: return launch_ring_op<DT, PTORED_MAX>(p, a, cu, s);
+    case PTORED_MIN: return launch_ring_op<DT, PTORED_MIN>(p, a, cu, s);
+    case PTORED_PROD: return launch_ring_op<DT, PTORED_PROD>(p, a, cu, s);
     default: return kLaunchNoKernel;
     }
 }
@@ -192,10 +201,10 @@ static int dispatch_dtype(const Plan& p, const KArgs& a, int cu, hipStream_t s) 
     if (p.accumulate) return dispatch_accumulate<DT, ES>(p, a, s);
     if (p.family == kFamCopy) return dispatch_copy<DT, ES>(p, a, cu, s);
     switch (p.op) {
-    case PTORED_SUM: return dispatch_op<DT, PTORED_SUM, ES>(p, a, cu, s);
-    case PTORED_MAX: return dispatch_op<DT, PTORED_MAX, ES>(p, a, cu, s);
-    case PTORED_MIN: return dispatch_op<DT, PTORED_MIN, ES>(p, a, cu, s);
-    case PTORED_PROD: return dispatch_op<DT, PTORED_PROD, ES>(p, a, cu, s);
+    case PTORED_SUM: return launch_op<DT, PTORED_SUM>(p, a, cu, s);
+    case PTORED_MAX: return launch_op<DT, PTORED_MAX>(p, a, cu, s);
+    case PTORED_MIN: return launch_op<DT, PTORED_MIN>(p, a, cu, s);
+    case PTORED_PROD: return launch_op<DT, PTORED_PROD>(p, a, cu, s);
     default: return kLaunchNoKernel;
     }
 }
