@@ -308,3 +308,11 @@ def test_tensor_wrappers_reject_bad_groups():
     with pytest.raises(ValueError):  # CPU tensors are not on a GPU
         crc.allreduce([a, torch.zeros(4, 8)])
     assert crc.ring_bounds(100, 4, "bf16") == [0, 32, 64, 80, 100]
+
+
+def test_c_consumer_program_compiles(tmp_path):
+    """The C program of the GPU test (tests/c_consumer_gpu.c) builds against the
+    header, the library and the oracle with warnings as errors."""
+    from tests.test_c_consumer_gpu import _build
+
+    assert os.path.exists(_build(tmp_path))
