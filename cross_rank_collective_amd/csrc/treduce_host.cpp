@@ -480,7 +480,7 @@ int plan_treduce(const void* const* srcs, int nranks, int root, const void* dst,
 void ring_bounds(int64_t count, int nranks, int dtype, int64_t* bounds) {
     bounds[0] = 0;
     for (int i = 1; i < nranks; ++i) {
-        // i * count fits: count < 2^60 / 64 is checked by the callers
+        // the product is formed in 128 bits; the quotient is at most count
         int64_t b = (int64_t)(((unsigned __int128)i * (uint64_t)count) / (uint64_t)nranks);
         if (esize_of(dtype) == 2) b = std::min<int64_t>(count, (b + 15) / 16 * 16);
         bounds[i] = b;
