@@ -16,6 +16,11 @@ import torch
 import oracle
 from tests import brute
 
+# NaN bit patterns and doubles beyond a format's range are cast on purpose.
+pytestmark = pytest.mark.filterwarnings(
+    "ignore:invalid value encountered in cast:RuntimeWarning",
+    "ignore:overflow encountered in cast:RuntimeWarning")
+
 DT = ["f32", "bf16", "f16", "i32"]
 FLOAT_DT = ["f32", "bf16", "f16"]
 STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16, "i32": np.int32}
