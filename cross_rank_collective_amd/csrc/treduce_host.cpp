@@ -165,7 +165,7 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         const uint64_t streams = p.family == kFamCopy ? 2u
                                  : mode == kModeAllreduce ? 2u * (uint64_t)nranks
                                                           : (uint64_t)nranks + 1u;
-        p.wgs_per_cu = wgs_per_cu_for(streams * slot_bytes);
+        p.wgs_per_cu = wgs_per_cu_for(streams * slot_bytes, mode == kModeAllreduce);
     }
     const int64_t vec = p.vec_elems;
     if (p.rows_mode) {
@@ -385,12 +385,13 @@ int facts_of_current_device(DeviceFacts& f) {
 }
 
 // The LDS reservation that lets exactly `wgs` workgroups share one CU:
-// more than lds_per_cu / (wgs + 1), at most lds_per_cu / wgs, on a 2 KiB
-// grid (coarser than the hardware's allocation unit), and within one
-// workgroup's limit; 0 when no such size exists.
+// more than lds_per_cu / (wgs + 1), at most lds_per_cu / wgs, in whole
+// allocation units, and within one workgroup's limit; 0 when no such size
+// exists (no whole number of units fits exactly `wgs`, as for 13 or 15).
 uint32_t cap_lds_bytes(const DeviceFacts& f, int wgs) {
     if (wgs < 1 || f.lds_per_cu <= 0) return 0;
-    const int64_t grain = 2048;
+    const int64_t grain = (int64_t)f.lds_per_cu / kLdsUnitsPerCu;
+    if (grain <= 0) return 0;
     const int64_t lds = (int64_t)f.lds_per_cu / wgs / grain * grain;
     if (lds * (wgs + 1) <= (int64_t)f.lds_per_cu || lds > (int64_t)f.lds_per_block) return 0;
     return (uint32_t)lds;
@@ -670,7 +671,7 @@ extern "C" int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, v
         if (st != PTORED_OK) return st;
         if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages) {
             if (p.wgs_per_cu > 0)  // the ring kernel moves one slot per thread
-                p.wgs_per_cu = wgs_per_cu_for((uint64_t)(nranks + 1) * kBlock * 16u);
+                p.wgs_per_cu = wgs_per_cu_for((uint64_t)(nranks + 1) * kBlock * 16u, false);
             return run_ring(p, srcs, dsts, bounds, count, stream);
         }
     }

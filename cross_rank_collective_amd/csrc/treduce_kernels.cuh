@@ -25,11 +25,12 @@
 // Block b takes tiles b, b+G, b+2G, ... of a grid of G blocks (the pages'
 // block-cyclic walk).  By default G equals the tile count -- one tile per
 // block, handed out in order by the hardware dispatcher, round-robin over
-// the XCDs, as blocks retire -- and the host keeps only 1-3 blocks resident
-// per CU (an LDS reservation), so the tiles in flight cover a compact
-// window of every buffer; a smaller persistent grid can be requested.
-// Within a tile, wave w owns U * 64 consecutive slots and lane l the slots
-// l, l+64, ..., so every wave instruction moves 1 KiB of one buffer.
+// the XCDs, as blocks retire -- and the host keeps only 3-16 blocks resident
+// per CU (an LDS reservation, by the bytes a tile moves), so the tiles in
+// flight cover a compact window of every buffer; a smaller persistent grid
+// can be requested.  A block is one wave: its U * 64 slots are consecutive
+// and lane l takes slots l, l+64, ..., so every wave instruction moves
+// 1 KiB of one buffer.
 //
 // Per slot a thread issues the loads of all N sources before it combines
 // anything -- the many waves in flight on a CU take the place of the pages'

@@ -131,15 +131,15 @@ int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int
 #define PTORED_FLAT_WALK 0x100u       /* 2-D region: slots numbered straight through the rows
                                          instead of row tiles */
 #define PTORED_FULL_OCCUPANCY 0x80u   /* let every CU hold as many workgroups as fit, instead of
-                                         the 1-3 per CU the automatic launch keeps resident */
+                                         the 3-16 per CU the automatic launch keeps resident */
 
 /* Launch choices of ptored_treduce_ex. */
 typedef struct ptored_tuning {
     uint32_t flags;          /* PTORED_FORCE_* and PTORED_NO_XCD_REMAP bits */
-    int32_t blocks_per_cu;   /* 0 = one workgroup per tile (default; 1-3 resident per compute
-                                unit, by the bytes a tile moves); > 0 = persistent grid of that
-                                many workgroups per compute unit, in per-XCD bands; < 0 =
-                                persistent grid at the kernel's occupancy */
+    int32_t blocks_per_cu;   /* 0 = one workgroup (one wave) per tile (default; 3-16 resident
+                                per compute unit, by the bytes a tile moves); > 0 = persistent
+                                grid of that many workgroups per compute unit, in per-XCD
+                                bands; < 0 = persistent grid at the kernel's occupancy */
     int64_t max_launch_bytes; /* split a call into launches that touch at most this many
                                  bytes of each buffer; 0 = auto (2^31) */
 } ptored_tuning;

@@ -130,16 +130,19 @@ def test_plan_paths():
 
 
 def test_plan_resident_workgroups():
-    """Workgroups kept resident per CU by one-tile-per-block launches, from
-    the bytes one tile moves: 3 up to 24 KiB, 2 up to 96 KiB, 1 beyond; no
-    limit for the element-wise kernel, persistent grids or on request."""
-    assert _plan(n=16, srcs=A[:16], dtype=3).wgs_per_cu == 2   # 17 x 4 KiB
-    assert _plan(n=8, srcs=A[:8], dtype=1).wgs_per_cu == 2     # 9 x 4 KiB
-    assert _plan(n=5, srcs=A[:5]).wgs_per_cu == 3              # 6 x 4 KiB
-    assert _plan(n=6, srcs=A[:6]).wgs_per_cu == 2              # 7 x 4 KiB
-    assert _plan(n=2, srcs=A[:2]).wgs_per_cu == 3              # 3 x 8 KiB (2 slots per thread)
-    assert _plan(n=1).wgs_per_cu == 3                          # copy: 2 x 8 KiB
-    assert _plan(n=17, srcs=A[:17]).wgs_per_cu == 1            # 18 x 8 KiB
+    """Workgroups (one wave each) kept resident per CU by one-tile-per-block
+    launches, from the bytes one tile moves (1 KiB per stream per slot row):
+    16 up to 5 KiB, 12 up to 7, 10 up to 13, 8 up to 17, 4 beyond; no limit
+    for the element-wise kernel, persistent grids or on request."""
+    assert _plan(n=16, srcs=A[:16], dtype=3).wgs_per_cu == 8   # 17 x 1 KiB
+    assert _plan(n=8, srcs=A[:8], dtype=1).wgs_per_cu == 10    # 9 x 1 KiB
+    assert _plan(n=12, srcs=A[:12]).wgs_per_cu == 10           # 13 x 1 KiB
+    assert _plan(n=6, srcs=A[:6]).wgs_per_cu == 12             # 7 x 1 KiB
+    assert _plan(n=5, srcs=A[:5]).wgs_per_cu == 12             # 6 x 1 KiB
+    assert _plan(n=4, srcs=A[:4]).wgs_per_cu == 16             # 5 x 1 KiB
+    assert _plan(n=2, srcs=A[:2]).wgs_per_cu == 12             # 3 x 2 KiB (2 slots per thread)
+    assert _plan(n=1).wgs_per_cu == 16                         # copy: 2 x 2 KiB
+    assert _plan(n=17, srcs=A[:17]).wgs_per_cu == 4            # 18 x 2 KiB
     assert _plan(srcs=[A[0], A[1] + 4]).wgs_per_cu == 0        # element-wise
     assert _plan(tuning=B.tuning(flags=B.PTORED_FULL_OCCUPANCY)).wgs_per_cu == 0
     assert _plan(tuning=B.tuning(blocks_per_cu=2)).wgs_per_cu == 0
@@ -177,23 +180,23 @@ def test_plan_walk_and_slots():
     info = _plan(rows=8, cols=10, ld=12, vr=7, vc=10)  # narrow rows: flattened, 3 slots/row
     assert (info.rows_mode, info.slots) == (2, 21)
     info = _plan(rows=8, cols=8, ld=8, vr=8, vc=8, tuning=B.tuning(flags=B.PTORED_FORCE_ROWS))
-    assert (info.rows_mode, info.slots) == (2, 16)  # 2 slots per row fill 1/128 of a chunk
-    # wide rows: row tiles (tile = row x column chunk) when a row's slots fill
-    # its chunks: 1000 f32 = 250 slots in one chunk of 256; flattened on request
+    assert (info.rows_mode, info.slots) == (2, 16)  # 2 slots per row fill 1/32 of a chunk
+    # wide rows: row tiles (tile = row x column chunk of 64 slots) when a row's
+    # slots fill its chunks: 1000 f32 = 250 slots in 4 chunks; flattened on request
     info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000)
     assert (info.rows_mode, info.slots) == (1, 60 * 250)
     flat = B.tuning(flags=B.PTORED_FLAT_WALK)
     info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000, tuning=flat)
     assert (info.rows_mode, info.slots) == (2, 60 * 250)
-    # 3 chunks of 256 slots for 513 slots: 513/768 of the threads busy -> flattened,
+    # 2 chunks of 64 slots for 65 slots: 65/128 of the threads busy -> flattened,
     # unless row tiles are forced
-    info = _plan(n=4, srcs=A[:4], rows=4, cols=2052, ld=2056, vr=4, vc=2052)
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=260, ld=264, vr=4, vc=260)
     assert info.rows_mode == 2
     rt = B.tuning(flags=B.PTORED_ROW_TILES)
-    info = _plan(n=4, srcs=A[:4], rows=4, cols=2052, ld=2056, vr=4, vc=2052, tuning=rt)
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=260, ld=264, vr=4, vc=260, tuning=rt)
     assert info.rows_mode == 1
     # 8 or more chunks per row: row tiles whatever the last chunk holds
-    info = _plan(n=4, srcs=A[:4], rows=4, cols=4 * 7 * 256 + 4, ld=7200, vr=4, vc=7172)
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=4 * 7 * 64 + 4, ld=1800, vr=4, vc=1796)
     assert info.rows_mode == 1
     # the LDS variant walks flattened
     lds = B.tuning(flags=B.PTORED_LDS_PINGPONG)
