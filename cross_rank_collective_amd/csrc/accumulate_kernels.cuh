@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const KArgs a) {
                     for (uint32_t e = 0; e < a.tail_bytes; e += ES)
                         atomic_add_elem<DT, ES>(d + off + e, load_elem<ES>(rs, off + e));
                 } else if (q - a.ntail < a.nhead) {  // row head: bytes [head_lo, 16)
-                    const uint32_t off = (q - a.ntail) * a.ld_bytes;
+                    const uint32_t off = (q - a.ntail) * a.ld_bytes + a.head_off;
                     for (uint32_t e = a.head_lo; e < 16u; e += ES)
                         atomic_add_elem<DT, ES>(d + off + e, load_elem<ES>(rs, off + e));
                 }

@@ -51,11 +51,14 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(const RingArgs a) {
                 store_elem<ES>(rd, off, acc.get());
             }
         } else {
-            const uint32_t nslots = first < end ? (end - first) >> 4 : 0u;
+            // slots numbered from the 1 KiB boundary at or below the first
+            // one, so that every wave's 1 KiB run is one aligned KiB
+            const uint32_t from = first & ~1023u;
+            const uint32_t nslots = first < end ? (end - from) >> 4 : 0u;
             const uint32_t base = local * (uint32_t)kBlock;
             if (base >= nslots) continue;  // a shorter segment's spare tile
-            const uint32_t j = base + threadIdx.x;
-            const uint32_t off[1] = {j < nslots ? first + j * 16u : kOutOfRange};
+            const uint32_t j = base + threadIdx.x, o = from + j * 16u;
+            const uint32_t off[1] = {j < nslots && o >= first ? o : kOutOfRange};
             u32x4 out[1];
             fold_slots<DT, OP, NR, 1>(src, n, off, out);
             store16(rd, off[0], out[0]);

@@ -445,16 +445,18 @@ __device__ __forceinline__ uint32_t logical_block(uint32_t b, uint32_t grid, boo
     return (b & 7u) * (grid >> 3) + (b >> 3);
 }
 
-// Byte offset of full slot s (16 bytes) in the flattened walks, or
-// kOutOfRange past the end.
+// Byte offset of numbered slot s (16 bytes) in the contiguous and flattened
+// walks, or kOutOfRange past the end and for the skipped slots before a
+// row's (or the span's) first full slot.
 template <int WALK>
 __device__ __forceinline__ uint32_t slot_offset(const KArgs& a, uint32_t s) {
     if (s >= a.nslots) return kOutOfRange;
     if constexpr (WALK == kWalkFlat) {
         const uint32_t row = fast_div(s, a.div_slots);
-        return row * a.ld_bytes + a.slot0_bytes + (s - row * a.slots_per_row) * 16u;
+        const uint32_t v = s - row * a.slots_per_row;
+        return v >= a.slot_skip ? row * a.ld_bytes + v * 16u : kOutOfRange;
     } else {
-        return a.slot0_bytes + s * 16u;
+        return s >= a.slot_skip ? s * 16u : kOutOfRange;
     }
 }
 
@@ -572,11 +574,11 @@ __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
     if constexpr (WALK == kWalkRowTiles) {
         const uint32_t row = fast_div(t, a.div_tiles);
         const uint32_t v0 = (t - row * a.tiles_per_row) * (uint32_t)(kBlock * U) + in_tile;
-        const uint32_t row_off = row * a.ld_bytes + a.slot0_bytes;
+        const uint32_t row_off = row * a.ld_bytes;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t v = v0 + (uint32_t)(u * 64);
-            off[u] = v < a.slots_per_row ? row_off + v * 16u : kOutOfRange;
+            off[u] = v < a.slots_per_row && v >= a.slot_skip ? row_off + v * 16u : kOutOfRange;
         }
     } else {
         const uint32_t base = t * (uint32_t)(kBlock * U) + in_tile;
@@ -774,14 +776,28 @@ __device__ __forceinline__ void row_head(const KArgs& a, uint32_t off) {
 }
 
 // One tail tile of the vector path: kBlock items, one per thread -- row
-// remainders (items [0, ntail)), then row heads (items [ntail, ntail + nhead)).
+// remainders (items [0, ntail)), row heads (the next nhead), then spill
+// slots (the next nspill): the last few whole slots of every row when they
+// would fill less than half of a row tile of their own, so each lane folds
+// one slot of a different row instead of most lanes of a tile idling.
 template <int DT, int OP, int ES, int NR, bool ALL>
 __device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
     const uint32_t q = t * (uint32_t)kBlock + threadIdx.x;
     if (q >= a.ntail) {
         const uint32_t h = q - a.ntail;
-        if (h >= a.nhead) return;
-        const uint32_t off = h * a.ld_bytes;
+        if (h >= a.nhead) {
+            const uint32_t k = h - a.nhead;
+            if (k >= a.nspill) return;
+            const uint32_t row = fast_div(k, a.div_spill);
+            const uint32_t v = a.spill_v0 + (k - row * a.spill_per_row);
+            const uint32_t off[1] = {row * a.ld_bytes + v * 16u};
+            u32x4 out[1];
+            fold_slots<DT, OP, NR, 1>([&](uint32_t r) { return make_rsrc(a.src[r], a.extent); },
+                                      a.nranks, off, out);
+            store_result<ALL>(a, make_rsrc(a.dst, a.extent), off[0], out[0]);
+            return;
+        }
+        const uint32_t off = h * a.ld_bytes + a.head_off;
         switch (a.head_lo) {  // uniform over the launch
         case 2: if constexpr (ES == 2) row_head<DT, OP, NR, 2, ALL>(a, off); break;
         case 4: row_head<DT, OP, NR, 4, ALL>(a, off); break;

@@ -21,10 +21,13 @@ struct FastDiv {
 };
 
 // Kernel arguments of one launch (passed by value; ~630 bytes of kernarg).
-// Offsets are bytes from each buffer's launch base, which is 16-byte aligned
-// on the vector path: when every buffer starts the same number of bytes past
-// a 16-byte boundary, the bases are moved back to that boundary and each row
-// begins with a head.
+// Offsets are bytes from each buffer's launch base.  On the vector path the
+// base is the coarsest boundary below the data -- 1 KiB, a 128-byte line or
+// 16 bytes -- at which every buffer starts at the same offset (and rows keep
+// it): the 16-byte slots of a row (or span) are numbered from that boundary,
+// the ones before the data are skipped, and a row that starts inside a slot
+// begins with a head -- so every wave's 1 KiB run of slots is one aligned
+// KiB, or at least whole cache lines.
 struct KArgs {
     // src[0] is the root's buffer, then the other ranks in ascending order:
     // the kernels fold src[0], src[1], ... in index order.
@@ -34,20 +37,25 @@ struct KArgs {
     uint32_t extent;         // bytes of every buffer this launch may touch (from its base)
     uint32_t main_tiles;     // tiles of full 16-byte slots
     uint32_t total_tiles;    // main tiles, then tail tiles of ragged elements
-    uint32_t nslots;         // full 16-byte slots
-    uint32_t slots_per_row;  // full slots per row (row walk)
+    uint32_t nslots;         // numbered 16-byte slots (the skipped ones included)
+    uint32_t slots_per_row;  // numbered slots per row (row walk)
     uint32_t ld_bytes;       // row pitch in bytes (row walk)
     uint32_t ntail;          // tail items: row remainders (vector path) or elements
     uint32_t tail_per_row;   // elements per row (element-wise row walk)
     uint32_t tail_bytes;     // bytes of every row remainder (vector path), < 16
     uint32_t tail_col_bytes; // byte offset in a row (or the span) of the remainder
     uint32_t tiles_per_row;  // column chunks per row (row tiles)
-    uint32_t slot0_bytes;    // byte offset of a row's first full slot (16 with a head, else 0)
+    uint32_t slot_skip;      // numbered slots of a row (or the span) before its first full slot
     uint32_t nhead;          // head items: a row's bytes before its first full slot
-    uint32_t head_lo;        // a head covers bytes [head_lo, 16) of its row's first slot
+    uint32_t head_off;       // byte offset in a row of the 16-byte block holding its head
+    uint32_t head_lo;        // a head covers bytes [head_lo, 16) of that block
+    uint32_t nspill;         // spill items: a row's last few slots, folded in tail tiles
+    uint32_t spill_per_row;  // spill slots per row (row tiles)
+    uint32_t spill_v0;       // numbered slot of a row's first spill slot
     FastDiv div_tiles;       // division by tiles_per_row
     FastDiv div_slots;       // division by slots_per_row
     FastDiv div_tail;        // division by tail_per_row
+    FastDiv div_spill;       // division by spill_per_row
     uint32_t xcd_remap;      // 1: per-XCD contiguous tile bands (persistent grids)
 };
 

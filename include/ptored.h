@@ -109,7 +109,9 @@ typedef enum ptored_status {
  * block, the pitch is a multiple of 16 bytes and every valid row reaches the
  * next 16-byte boundary, the 16-byte vector kernels still run (each row's
  * bytes before that boundary folded as a head); otherwise misaligned data
- * selects an element-wise kernel.
+ * selects an element-wise kernel.  Buffers that also share their offset
+ * within 1 KiB (or a 128-byte line) are walked in aligned 1 KiB runs (or
+ * whole lines) whatever that offset.
  */
 int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int64_t rows,
                    int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
@@ -166,8 +168,11 @@ typedef struct ptored_plan_info {
     int64_t launches;      /* kernel launches the call is split into */
     int32_t wgs_per_cu;    /* workgroups kept resident per CU by one-tile-per-block
                               launches large enough to fill them; 0 = as many as fit */
-    int32_t lead;          /* vector path: bytes past a 16-byte boundary at which every
-                              buffer starts (each row then begins with a head) */
+    int32_t lead;          /* vector path: bytes past the slot origin at which every buffer
+                              starts -- the coarsest of a 1 KiB, 128-byte or 16-byte
+                              boundary at which every buffer (and, for rows, the pitch)
+                              has the same offset; a row starting inside a 16-byte block
+                              begins with a head */
 } ptored_plan_info;
 
 /* Validate like ptored_treduce_ex and describe the launch it would make,

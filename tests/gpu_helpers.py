@@ -26,7 +26,7 @@ class DevBuf:
     (for misaligned pointers), surrounded by guard bands of one fill byte."""
 
     def __init__(self, nbytes: int, offset: int = 0, fill: int = 0xFF):
-        assert 0 <= offset < 256
+        assert 0 <= offset < 2048
         self.nbytes = nbytes
         self.start = GUARD + offset
         self.t = torch.full((GUARD + offset + nbytes + GUARD,), fill, dtype=torch.uint8,

@@ -174,6 +174,39 @@ def test_plan_common_lead():
     assert info.launches == 3
 
 
+def test_plan_line_origin():
+    """Slots are numbered from the coarsest of a 1 KiB, 128-byte or 16-byte
+    boundary at which every buffer (and, for rows, the pitch) has the same
+    offset; lead = that offset, with heads when it is inside a 16-byte block."""
+    info = _plan(srcs=[A[0] + 16, A[1] + 144], dst=D + 400)        # 16 mod 128
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 16)
+    info = _plan(srcs=[A[0] + 100, A[1] + 100], dst=D + 100)       # 100 mod 128: a head
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 100)
+    info = _plan(srcs=[A[0] + 16, A[1] + 32], dst=D + 16)          # only 0 mod 16 in common
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 0)
+    info = _plan(srcs=[A[0] + 36, A[1] + 52], dst=D + 4)           # only 4 mod 16
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 4)
+    # 2-D: a pitch of 512 bytes keeps the line offset, one of 48 bytes does not
+    info = _plan(srcs=[A[0] + 36, A[1] + 36], dst=D + 36, rows=8, cols=100, ld=128, vr=8,
+                 vc=100)
+    assert (B.PATHS[info.path], info.rows_mode != 0, info.lead) == ("vec_fixed", True, 36)
+    info = _plan(srcs=[A[0] + 36, A[1] + 36], dst=D + 36, rows=8, cols=10, ld=12, vr=8, vc=10)
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 4)
+    info = _plan(srcs=[A[0] + 528, A[1] + 1552], dst=D + 528)      # 528 mod 1024
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 528)
+    info = _plan(srcs=[A[0] + 528, A[1] + 528], dst=D + 528, rows=8, cols=256, ld=256, vr=8,
+                 vc=250)                                           # 1 KiB pitch keeps it
+    assert (info.rows_mode != 0, info.lead) == (True, 528)
+    info = _plan(srcs=[A[0] + 528, A[1] + 528], dst=D + 528, rows=8, cols=100, ld=128, vr=8,
+                 vc=100)                                           # 512 B pitch: the line
+    assert info.lead == 16
+    # launch windows that lie wholly before the data are not launched: bytes
+    # [100, 356) in windows of 32 meet windows 3 .. 11
+    info = _plan(srcs=[A[0] + 100, A[1] + 100], dst=D + 100, rows=1, cols=64, ld=64, vr=1,
+                 vc=64, tuning=B.tuning(max_launch_bytes=32))
+    assert (info.lead, info.launches) == (100, 9)
+
+
 def test_plan_walk_and_slots():
     info = _plan(rows=8, cols=8, ld=8, vr=8, vc=8)  # contiguous f32
     assert (info.rows_mode, info.vec_elems, info.slots, info.launches) == (0, 4, 16, 1)
@@ -188,12 +221,17 @@ def test_plan_walk_and_slots():
     flat = B.tuning(flags=B.PTORED_FLAT_WALK)
     info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000, tuning=flat)
     assert (info.rows_mode, info.slots) == (2, 60 * 250)
-    # 2 chunks of 64 slots for 65 slots: 65/128 of the threads busy -> flattened,
-    # unless row tiles are forced
-    info = _plan(n=4, srcs=A[:4], rows=4, cols=260, ld=264, vr=4, vc=260)
+    # 100 slots: one whole chunk of 64 and a last one 36/64 full (more than half,
+    # so it stays a tile): 100/128 of the threads busy -> flattened, unless row
+    # tiles are forced
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=400, ld=404, vr=4, vc=400)
     assert info.rows_mode == 2
     rt = B.tuning(flags=B.PTORED_ROW_TILES)
-    info = _plan(n=4, srcs=A[:4], rows=4, cols=260, ld=264, vr=4, vc=260, tuning=rt)
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=400, ld=404, vr=4, vc=400, tuning=rt)
+    assert info.rows_mode == 1
+    # 65 slots: one whole chunk, the last slot of each row spills into the tail
+    # tiles, so the row tiles are full -> row tiles
+    info = _plan(n=4, srcs=A[:4], rows=4, cols=260, ld=264, vr=4, vc=260)
     assert info.rows_mode == 1
     # 8 or more chunks per row: row tiles whatever the last chunk holds
     info = _plan(n=4, srcs=A[:4], rows=4, cols=4 * 7 * 64 + 4, ld=1800, vr=4, vc=1796)

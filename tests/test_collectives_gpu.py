@@ -84,10 +84,11 @@ def test_allreduce_in_place_random(dtype):
 @pytest.mark.parametrize("dtype", DT)
 def test_collectives_common_lead(dtype):
     """Allreduce, ring reduce-scatter and push-with-add over buffers that all
-    start the same number of bytes past a 16-byte boundary."""
+    start the same number of bytes past a 16-byte boundary, in every other
+    case at one offset within a 128-byte line."""
     rng = np.random.default_rng({"f32": 61, "bf16": 62, "f16": 63, "i32": 64}[dtype])
     es = ESIZE[dtype]
-    for case in range(8):
+    for case in range(12):
         lead = int(rng.choice(list(range(es, 16, es))))
         n = int(rng.choice([2, 5, 8, 16]))
         rows, cols = int(rng.integers(2, 30)), int(rng.integers(16, 900))
@@ -95,7 +96,13 @@ def test_collectives_common_lead(dtype):
         vr, vc = int(rng.integers(1, rows + 1)), int(rng.integers(8, cols + 1))
         size = (rows - 1) * ld + cols
         op = OPS[case % 4]
-        offs = [lead + 16 * int(rng.integers(0, 3)) for _ in range(n)]
+        if case % 2:  # one offset within a 128-byte line for every buffer
+            common = lead + 16 * int(rng.integers(0, 8))
+            offs = [common] * n
+            doff = lambda: common  # noqa: E731
+        else:  # one offset within a 16-byte block only
+            offs = [lead + 16 * int(rng.integers(0, 3)) for _ in range(n)]
+            doff = lambda: lead + 16 * int(rng.integers(0, 3))  # noqa: E731
         say(f"lead collectives#{case} {dtype} {op} lead={lead} N={n} {rows}x{cols} ld={ld} "
             f"valid={vr}x{vc}")
         # allreduce in place
@@ -114,8 +121,7 @@ def test_collectives_common_lead(dtype):
         # ring reduce-scatter over the whole stream
         count = size
         sb = _upload(srcs, offs)
-        db = [DevBuf(count * es, lead + 16 * int(rng.integers(0, 3)), fill=0xFF)
-              for _ in range(n)]
+        db = [DevBuf(count * es, doff(), fill=0xFF) for _ in range(n)]
         st = B.ptored_reduce_scatter_ring([b.ptr for b in sb], n, [b.ptr for b in db], count,
                                           B.DTYPES[dtype], B.OPS[op], None, _stream())
         torch.cuda.synchronize()
@@ -130,7 +136,7 @@ def test_collectives_common_lead(dtype):
         fsrcs = [_finite_values(dtype, rng, size) for _ in range(n)]
         d0 = _finite_values(dtype, rng, size)
         sb = _upload(fsrcs, offs)
-        dd = _upload([d0], [lead])[0]
+        dd = _upload([d0], [doff()])[0]
         st = B.ptored_accumulate_add([b.ptr for b in sb], n, dd.ptr, rows, cols, ld, vr, vc,
                                      B.DTYPES[dtype], None, _stream())
         torch.cuda.synchronize()

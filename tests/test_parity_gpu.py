@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from cross_rank_collective_amd import binding as B
 from cross_rank_collective_amd import workloads as W
 from tests.gpu_helpers import (compare, oracle_reduce, run_gpu, say, sentinel, valid_mask,
@@ -179,6 +180,104 @@ def test_common_lead_keeps_vector_path(dtype):
             _check(srcs, dtype, op, root, rows, cols, ld, vr, vc, dst, bufs, alias=alias,
                    label=label)
             case += 1
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_common_line_offset(dtype):
+    """Every buffer at the same byte offset (views at one element offset into
+    larger allocations): slots numbered from the coarsest of a 1 KiB, 128-byte
+    or 16-byte boundary that the pitch keeps, the ones before the data
+    skipped, a head when the offset is inside a 16-byte block.  Every walk,
+    windows, the LDS variant, in place."""
+    rng = np.random.default_rng({"f32": 171, "bf16": 172, "f16": 173, "i32": 174}[dtype])
+    es = ESIZE[dtype]
+    offsets = [o for o in (es, 16, 16 + es, 36, 64, 100, 124, 126, 132, 520, 1020, 1022)
+               if o % es == 0]
+    shapes = LEAD_SHAPES[:5] + [(33, 1000, 1024, 31, 999), (7, 3000, 3072, 7, 2999)]
+    variants = [("auto", 0, 0), ("flat", B.PTORED_FORCE_ROWS | B.PTORED_FLAT_WALK, 0),
+                ("row_tiles", B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES, 0),
+                ("lds", B.PTORED_LDS_PINGPONG, 0), ("windows", 0, 1008),
+                ("windows_16", 0, 16)]
+    case = 0
+    for rows, cols, ld, vr, vc in shapes:
+        for vi, (vname, flags, mlb) in enumerate(variants):
+            off = offsets[(case * 5 + vi) % len(offsets)]
+            n = int(rng.choice([1, 2, 5, 8, 16]))
+            root = int(rng.integers(0, n))
+            op = OPS[case % 4]
+            alias = int(rng.integers(0, n)) if case % 7 == 6 else -1
+            size = (rows - 1) * ld + cols
+            if mlb == 16 and size * es > 1 << 16:
+                continue  # 16-byte windows: small buffers only
+            srcs = [_rand_elems(dtype, rng, size) for _ in range(n)]
+            t = B.tuning(flags=flags, max_launch_bytes=mlb)
+            label = f"line#{case} off={off} {vname} {rows}x{cols} ld={ld} valid={vr}x{vc} N={n}"
+            st_plan, info = B.ptored_treduce_plan(
+                [0x1000000 + off] * n, n, root, 0x9000000 + off, rows, cols, ld, vr, vc,
+                B.DTYPES[dtype], B.OPS[op], t)
+            assert st_plan == 0
+            contig = (vc == ld or vr == 1) and not flags & B.PTORED_FORCE_ROWS
+            if B.PATHS[info.path] != "elementwise":
+                origin = next(a for a in (1024, 128, 16) if contig or (ld * es) % a == 0)
+                assert info.lead == off % origin, label
+            dst, st, bufs = run_gpu(srcs, dtype, op, root, rows, cols, ld, vr, vc,
+                                    offsets=[off] * n, dst_offset=off, tuning=t, alias=alias,
+                                    label=label)
+            assert st == 0, B.ptored_status_string(st)
+            _check(srcs, dtype, op, root, rows, cols, ld, vr, vc, dst, bufs, alias=alias,
+                   label=label)
+            case += 1
+
+
+# Rows whose last few whole slots spill into the tail tiles (fewer than half a
+# row tile past the last whole one), with and without a lead: (rows, cols,
+# ld, valid_rows, valid_cols, byte offset of every buffer).
+SPILL_SHAPES = [
+    (37, 1040, 1048, 37, 1040, 0),    # f32: 260 slots = 4 tiles + 4; 16-bit: 2 + 2
+    (9, 1040, 1088, 9, 1036, 0),      # remainder bytes after the spill slots
+    (4000, 272, 288, 4000, 260, 64),  # one whole tile and a short spill, many rows
+    (61, 12288, 12288, 61, 12287, 64),  # the ragged f16 shape at a 64-byte offset
+    (5, 300, 320, 5, 260, 36),        # a head, whole tiles, spill and a remainder
+]
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_row_tiles_with_spill_slots(dtype):
+    """Row tiles whose rows end a few slots past their last whole tile: those
+    slots folded in the tail tiles, one per lane across rows.  Reduction and
+    allreduce, unrolled, two-slot (N <= 2) and runtime rank loops."""
+    rng = np.random.default_rng({"f32": 81, "bf16": 82, "f16": 83, "i32": 84}[dtype])
+    es = ESIZE[dtype]
+    for case, (rows, cols, ld, vr, vc, off) in enumerate(SPILL_SHAPES):
+        if vc > cols:
+            continue
+        for n, flags in ((2, 0), (5, B.PTORED_ROW_TILES | B.PTORED_FORCE_ROWS),
+                         (17, B.PTORED_FORCE_ROWS)):
+            if rows * ld * n > 30_000_000:
+                continue
+            root = int(rng.integers(0, n))
+            op = OPS[(case + n) % 4]
+            size = (rows - 1) * ld + cols
+            srcs = [_rand_elems(dtype, rng, size) for _ in range(n)]
+            t = B.tuning(flags=flags)
+            label = f"spill#{case} N={n} {rows}x{cols} ld={ld} valid={vr}x{vc} off={off}"
+            o = off - off % es
+            dst, st, bufs = run_gpu(srcs, dtype, op, root, rows, cols, ld, vr, vc,
+                                    offsets=[o] * n, dst_offset=o, tuning=t, label=label)
+            assert st == 0, B.ptored_status_string(st)
+            _check(srcs, dtype, op, root, rows, cols, ld, vr, vc, dst, bufs, label=label)
+            # the in-place allreduce on the same buffers
+            st = B.ptored_allreduce([b.ptr for b in bufs], n, root, rows, cols, ld, vr, vc,
+                                    B.DTYPES[dtype], B.OPS[op], t,
+                                    torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            assert st == 0, B.ptored_status_string(st)
+            want = [x[:size].copy() for x in srcs]
+            oracle.allreduce_inplace(want, root=root, dtype=dtype, op=op, rows=rows, cols=cols,
+                                     ld=ld, valid_rows=vr, valid_cols=vc)
+            for r, b in enumerate(bufs):
+                assert compare(dtype, b.download(dtype), want[r]).all(), (label, "allreduce", r)
+                assert b.guards_intact(), (label, r)
 
 
 MEDIUM = [

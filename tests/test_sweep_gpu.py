@@ -69,14 +69,17 @@ def _shape(rng, es):
 
 
 def _offsets(rng, es, n):
-    """Byte offsets of n buffers (+ one more for a dst): aligned, one shared
-    lead, or each its own."""
-    kind = rng.choice([0, 0, 1, 1, 2])
+    """Byte offsets of n buffers (+ one more for a dst): on the 16-byte grid,
+    one shared offset within a 16-byte block, one shared offset within
+    1 KiB, or each its own."""
+    kind = rng.choice([0, 0, 1, 1, 2, 2, 3])
     if kind == 0:
-        return [16 * int(rng.integers(0, 4)) for _ in range(n + 1)]
+        return [16 * int(rng.integers(0, 8)) for _ in range(n + 1)]
     if kind == 1:
         lead = int(rng.choice(list(range(es, 16, es))))
-        return [lead + 16 * int(rng.integers(0, 4)) for _ in range(n + 1)]
+        return [lead + 16 * int(rng.integers(0, 8)) for _ in range(n + 1)]
+    if kind == 2:
+        return [es * int(rng.integers(0, 1024 // es))] * (n + 1)
     return [es * int(rng.integers(0, 32)) for _ in range(n + 1)]
 
 
