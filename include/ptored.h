@@ -133,7 +133,11 @@ int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int
 #define PTORED_FLAT_WALK 0x100u       /* 2-D region: slots numbered straight through the rows
                                          instead of row tiles */
 #define PTORED_FULL_OCCUPANCY 0x80u   /* let every CU hold as many workgroups as fit, instead of
-                                         the 3-16 per CU the automatic launch keeps resident */
+                                         the 3-16 per CU the automatic launch keeps resident
+                                         by reserving LDS it does not use -- a reservation
+                                         that also keeps kernels running concurrently on
+                                         other streams off those CUs' LDS; set this when the
+                                         reduction overlaps such kernels */
 
 /* Launch choices of ptored_treduce_ex. */
 typedef struct ptored_tuning {
