@@ -18,8 +18,9 @@
 //   contiguous  the valid rows follow each other without a gap: one span,
 //               tiles of consecutive slots;
 //   row tiles   the pages' 2-D sliding chunk walk: tile (r, c) is column
-//               chunk c of row r, the last chunk of a row masked -- used
-//               when rows are wide enough to keep the threads busy;
+//               chunk c of row r, the last chunk of a row masked (or, when
+//               it would be at most half full, left to the tail tiles) --
+//               used when rows are wide enough to keep the threads busy;
 //   flattened   narrow rows: slots numbered row-major straight through the
 //               rectangle, the row found by a multiply-high division.
 // Block b takes tiles b, b+G, b+2G, ... of a grid of G blocks (the pages'
@@ -49,16 +50,20 @@
 // stream than non-temporal or default stores (the in-place allreduce's N
 // store-backs add nt).
 //
-// Ragged edges.  Full 16-byte slots form the main tiles; the valid bytes
-// after the last full slot of each row (fewer than 16), or at the end of a
-// contiguous span, form separate tail tiles -- placed before the main tiles
-// in the grid, so their scattered accesses overlap the streaming -- in
-// which one thread moves one row's remainder with at most two exact-size
-// accesses per buffer (12 + 2 bytes for seven 16-bit elements), so nothing
-// outside the valid rectangle is touched.  The main tiles are therefore
-// branch-free.  The element-wise
-// path (data not 16-byte aligned) has no main tiles: its tail tiles carry
-// every element of the rectangle, one element per access.
+// Ragged edges.  Full 16-byte slots form the main tiles.  They are numbered
+// from an aligned origin below the data (1 KiB, 128 bytes or 16 bytes, the
+// coarsest at which every buffer has the same offset), so every wave's run
+// is aligned; the slots before the data are skipped.  Separate tail tiles
+// -- placed before the main tiles in the grid, so their scattered accesses
+// overlap the streaming -- carry, one item per thread: a row's valid bytes
+// after its last full slot (fewer than 16, at most two exact-size accesses
+// per buffer, e.g. 12 + 2 bytes for seven 16-bit elements), a row's head
+// (its bytes before the first 16-byte boundary when the data starts inside
+// a slot, at most three aligned accesses), and a row's last few full slots
+// when they would fill at most half of a row tile.  Nothing outside the
+// valid rectangle is touched, and the main tiles are branch-free.  The
+// element-wise path (buffers at different offsets) has no main tiles: its
+// tail tiles carry every element of the rectangle, one element per access.
 //
 // Combines on gfx950 (element type kept after every step):
 //   f32  sum v_add_f32, prod v_mul_f32, max/min v_maximum3_f32 / v_minimum3_f32
@@ -563,9 +568,9 @@ __device__ __forceinline__ void fold_slots(SrcFn src, uint32_t n, const uint32_t
 
 // One main tile: U full 16-byte slots per thread, NR sources.  Row tiles:
 // tile t is column chunk c of row r (t = r * tiles_per_row + c, split on
-// the scalar unit), so every wave's 1 KiB run starts 1 KiB into a row and
-// never shares a cache line with another wave; flattened walks number the
-// slots straight through.
+// the scalar unit), so every wave's 1 KiB run starts a whole number of KiB
+// past the row's slot origin and never shares a cache line with another
+// wave; the other walks number the slots straight through.
 template <int DT, int OP, int NR, int U, int WALK, bool ALL>
 __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
