@@ -343,6 +343,7 @@ def main() -> int:
     set_ptrs = [[t.data_ptr() for t in srcs_k] for srcs_k, _ in sets]
     residency = "hbm" if nsets * set_bytes >= ROTATE_BYTES else "cache-resident"
     launches = 1
+    launch = None
     if mode == "treduce":
         st, info = B.ptored_treduce_plan([t.data_ptr() for t in src_t], w.nranks, w.root,
                                          dst_t.data_ptr(), w.rows, w.cols, w.ld, w.valid_rows,
@@ -350,6 +351,13 @@ def main() -> int:
         if st != 0:
             raise RuntimeError(B.ptored_status_string(st))
         launches = int(info.launches)
+        # how the library launches the call (its own plan, no HIP call)
+        launch = {"kernel_family": B.PATHS[info.path],
+                  "walk": {0: "contiguous", 1: "row_tiles", 2: "flattened"}[info.rows_mode],
+                  "workgroup_threads": B.PTORED_WORKGROUP_THREADS,
+                  "slots_per_thread": int(info.slots_per_thread),
+                  "workgroups_per_cu": int(info.wgs_per_cu) or "all that fit",
+                  "lead_bytes": int(info.lead), "launches": launches}
 
     def call(k):
         srcs_k, dst_k = sets[k]
@@ -427,6 +435,7 @@ def main() -> int:
             "values": w.recipe, "mode": mode, "algorithmic_bytes_per_step": algo_bytes,
             "launches_per_step": launches, "input_sets": nsets, "residency": residency,
         },
+        "launch": launch,
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "elements_per_s": round(elems_s, 1),
         "roofline": {

@@ -40,6 +40,9 @@ PTORED_SEGMENT_LAUNCHES = 0x40
 PTORED_FULL_OCCUPANCY = 0x80
 PTORED_FLAT_WALK = 0x100
 
+PTORED_MAX_RANKS = 64
+PTORED_WORKGROUP_THREADS = 64  # threads per workgroup of the kernels (one wave)
+
 PATHS = {0: "none", 1: "copy", 2: "vec_fixed", 3: "vec_runtime", 4: "elementwise"}
 
 

@@ -137,6 +137,7 @@ enum LaunchStatus : int {
 // four-wave ones (two-wave ones fell in between) on the large reductions,
 // the allreduce, the ring and the element-wise path.
 constexpr int kBlock = 64;
+static_assert(kBlock == PTORED_WORKGROUP_THREADS, "the header states the workgroup size");
 
 // Unroll (16-byte slots per thread per main tile).  Bandwidth sweeps on
 // MI355X over tiles of 1 to 16 slots per thread: the smallest tiles were

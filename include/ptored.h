@@ -43,6 +43,9 @@ extern "C" {
 #define PTORED_ABI_VERSION 2
 /* Largest number of ranks (source buffers) one call accepts. */
 #define PTORED_MAX_RANKS 64
+/* Threads in one workgroup of the library's kernels: one 64-wide wave.
+ * Informative; the plan's resident-workgroup counts are in these units. */
+#define PTORED_WORKGROUP_THREADS 64
 
 /* Element type.  One type for every source and for dst ([TREDUCE] §3.1). */
 typedef enum ptored_dtype {

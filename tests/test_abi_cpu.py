@@ -357,3 +357,24 @@ def test_c_consumer_program_compiles(tmp_path):
     from tests.test_c_consumer_gpu import _build
 
     assert os.path.exists(_build(tmp_path))
+
+
+def test_binding_constants_match_the_header():
+    """Every numeric #define of include/ptored.h that the binding mirrors has
+    the same value there (flags, limits, the workgroup size)."""
+    import re
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    text = open(os.path.join(os.path.dirname(here), "include", "ptored.h")).read()
+    defines = dict(re.findall(r"^#define (PTORED_\w+) (0x[0-9a-fA-F]+|\d+)", text, re.M))
+    assert "PTORED_WORKGROUP_THREADS" in defines and "PTORED_FLAT_WALK" in defines
+    checked = 0
+    for name, value in defines.items():
+        if hasattr(B, name):
+            assert getattr(B, name) == int(value.rstrip("uU"), 0), name
+            checked += 1
+    assert checked == 11  # nine flags, the rank limit and the workgroup size
+    paths = {int(v): k[len("PTORED_PATH_"):].lower() for k, v in defines.items()
+             if k.startswith("PTORED_PATH_")}
+    assert paths == {0: "none", 1: "copy", 2: "vec_fixed", 3: "vec_runtime", 4: "elementwise"}
+    assert B.PATHS == paths
