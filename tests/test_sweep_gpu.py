@@ -8,6 +8,8 @@ the allreduce and the reduce-scatter, exact for i32 push-with-add; cells
 outside the valid rectangle, guard bands and sources untouched.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -28,6 +30,8 @@ FLAG_SETS = [0, 0, 0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_FORCE_ROWS,
              B.PTORED_FORCE_RUNTIME_N | B.PTORED_FULL_OCCUPANCY,
              B.PTORED_LDS_PINGPONG | B.PTORED_FORCE_ROWS | B.PTORED_FLAT_WALK]
 MAX_ELEMS = 40000  # per buffer
+# PTORED_SWEEP_SCALE=k draws k times as many calls per test (default 1).
+SCALE = max(1, int(os.environ.get("PTORED_SWEEP_SCALE", "1")))
 
 
 @pytest.fixture(autouse=True, scope="module")
@@ -101,7 +105,7 @@ def _tstr(t):
 @pytest.mark.parametrize("chunk", range(8))
 def test_sweep_treduce(chunk):
     rng = np.random.default_rng(9100 + chunk)
-    for case in range(100):
+    for case in range(100 * SCALE):
         dtype = DT[int(rng.integers(0, 4))]
         op = OPS[int(rng.integers(0, 4))]
         es = ESIZE[dtype]
@@ -135,7 +139,7 @@ def _upload(arrs, offs, fill=0xA5):
 
 def test_sweep_allreduce():
     rng = np.random.default_rng(9200)
-    for case in range(200):
+    for case in range(200 * SCALE):
         dtype = DT[int(rng.integers(0, 4))]
         op = OPS[int(rng.integers(0, 4))]
         es = ESIZE[dtype]
@@ -167,7 +171,7 @@ def test_sweep_allreduce():
 
 def test_sweep_reduce_scatter_ring():
     rng = np.random.default_rng(9300)
-    for case in range(200):
+    for case in range(200 * SCALE):
         dtype = DT[int(rng.integers(0, 4))]
         op = OPS[int(rng.integers(0, 4))]
         es = ESIZE[dtype]
@@ -208,7 +212,7 @@ def test_sweep_reduce_scatter_ring():
 def test_sweep_accumulate_i32():
     """i32 push-with-add: wrapping sums are the same in any order, so exact."""
     rng = np.random.default_rng(9400)
-    for case in range(100):
+    for case in range(100 * SCALE):
         n = int(rng.choice(RANKS))
         rows, cols, ld, vr, vc = _shape(rng, 4)
         offs = _offsets(rng, 4, n)
