@@ -224,28 +224,32 @@ def test_accumulate_add_over_2gib():
     assert bool((dst == want).all())
 
 
-def test_common_lead_full_size():
-    """n16_i32_4096x4096 with every buffer 4 bytes past a 16-byte boundary (the
-    vector path with a head): whole result against the wrapped sum, sampled
-    windows against the oracle."""
+@pytest.mark.parametrize("skip", [1, 132])
+def test_common_lead_full_size(skip):
+    """n16_i32_4096x4096 with every buffer `skip` elements past its allocation's
+    start (4 bytes: a head in the first 16-byte block; 528 bytes: 33 skipped
+    slots before it, numbered from the 1 KiB boundary): whole result against
+    the wrapped sum, sampled windows against the oracle."""
     w = W.WORKLOADS["n16_i32_4096x4096"]
     n = w.buffer_elems
-    say("large common lead n16_i32_4096x4096 +4 bytes")
-    raw = _sources("i32", n + 4, w.nranks, 7800)  # one spare element in front of each
-    srcs = [t[1:] for t in raw]                   # 4 bytes past the allocation's alignment
-    dbuf = _sentinel_dev("i32", n + 4 + PAD)
-    dst = dbuf[1:]
+    say(f"large common offset n16_i32_4096x4096 +{4 * skip} bytes")
+    raw = _sources("i32", n + skip, w.nranks, 7800)  # spare elements in front of each
+    srcs = [t[skip:] for t in raw]
+    dbuf = _sentinel_dev("i32", n + skip + PAD)
+    dst = dbuf[skip:]
     st, info = B.ptored_treduce_plan([t.data_ptr() for t in srcs], w.nranks, 0, dst.data_ptr(),
                                      w.rows, w.cols, w.ld, w.valid_rows, w.valid_cols,
                                      B.DTYPES["i32"], B.OPS["sum"])
-    assert st == 0 and info.lead == 4 and B.PATHS[info.path] == "vec_fixed"
+    assert st == 0 and B.PATHS[info.path] == "vec_fixed"
+    if all(t.data_ptr() % 1024 == 4 * skip % 1024 for t in srcs + [dst]):
+        assert info.lead == 4 * skip
     st = B.ptored_treduce([t.data_ptr() for t in srcs], w.nranks, 0, dst.data_ptr(), w.rows,
                           w.cols, w.ld, w.valid_rows, w.valid_cols, B.DTYPES["i32"],
                           B.OPS["sum"], _stream())
     torch.cuda.synchronize()
     assert st == 0, B.ptored_status_string(st)
     assert bool((dst[:n] == _wrapped_sum([t[:n] for t in srcs])).all())
-    assert int(dbuf[0]) == -1 and bool((dst[n:] == -1).all())
+    assert bool((dbuf[:skip] == -1).all()) and bool((dst[n:] == -1).all())
     rng = np.random.default_rng(7801)
     _check_samples(srcs, dst, _samples(n, [], rng), "i32", "sum", root=0)
 
