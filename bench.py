@@ -81,6 +81,8 @@ def algorithmic_bytes(w, mode: str) -> int:
 def traffic_path(workload: str, op: str, mode: str) -> str:
     suffix = "" if mode == "treduce" else f"_{mode}"
     return os.path.join(PROFILES, f"traffic_{workload}_{op}{suffix}.txt")
+
+
 CSRC = os.path.join(ROOT, "cross_rank_collective_amd", "csrc")
 
 
