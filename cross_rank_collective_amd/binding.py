@@ -201,6 +201,12 @@ def _torch_dtype_code(t) -> int:
     return _dtype_code(t.dtype)
 
 
+def _op_code(op: str) -> int:
+    if op not in OPS:
+        raise ValueError(f"unsupported op {op!r}; expected sum, max, min or prod")
+    return OPS[op]
+
+
 def _geometry(t) -> Tuple[int, int, int]:
     if t.dim() == 1:
         return 1, t.shape[0], t.shape[0]
@@ -248,12 +254,15 @@ def treduce(srcs, dst, op: str = "sum", root: int = 0,
     if len(srcs) == 0:
         raise ValueError("treduce needs at least one source")
     dt = _torch_dtype_code(dst)
+    opc = _op_code(op)
     rows, cols, ld = _check_group(list(srcs) + [dst], dst, "tensor")
     vr, vc = (rows, cols) if valid is None else valid
+    if vr == 0 or vc == 0:
+        return  # an empty rectangle writes nothing (empty tensors have no storage)
     handle = _stream_handle(stream, dst.device)
     with torch.cuda.device(dst.device):
         _raise_on(ptored_treduce_ex([s.data_ptr() for s in srcs], len(srcs), root,
-                                    dst.data_ptr(), rows, cols, ld, vr, vc, dt, OPS[op], tuning,
+                                    dst.data_ptr(), rows, cols, ld, vr, vc, dt, opc, tuning,
                                     handle))
 
 
@@ -266,12 +275,15 @@ def allreduce(bufs, op: str = "sum", root: int = 0, valid: Optional[Tuple[int, i
     if len(bufs) == 0:
         raise ValueError("allreduce needs at least one buffer")
     dt = _torch_dtype_code(bufs[0])
+    opc = _op_code(op)
     rows, cols, ld = _check_group(bufs, bufs[0], "buffer")
     vr, vc = (rows, cols) if valid is None else valid
+    if vr == 0 or vc == 0:
+        return
     handle = _stream_handle(stream, bufs[0].device)
     with torch.cuda.device(bufs[0].device):
         _raise_on(ptored_allreduce([b.data_ptr() for b in bufs], len(bufs), root, rows, cols,
-                                   ld, vr, vc, dt, OPS[op], tuning, handle))
+                                   ld, vr, vc, dt, opc, tuning, handle))
 
 
 def ring_bounds(count: int, nranks: int, dtype) -> list:
@@ -301,11 +313,14 @@ def reduce_scatter_ring(srcs, dsts, op: str = "sum", tuning: Optional[ptored_tun
         if not t.is_cuda or t.device != ref.device:
             raise ValueError("every stream must be on the same GPU")
     dt = _torch_dtype_code(ref)
+    opc = _op_code(op)
+    if ref.numel() == 0:
+        return
     handle = _stream_handle(stream, ref.device)
     with torch.cuda.device(ref.device):
         _raise_on(ptored_reduce_scatter_ring([s.data_ptr() for s in srcs], len(srcs),
                                              [d.data_ptr() for d in dsts], ref.numel(), dt,
-                                             OPS[op], tuning, handle))
+                                             opc, tuning, handle))
 
 
 def accumulate_add(srcs, dst, valid: Optional[Tuple[int, int]] = None,
@@ -320,6 +335,8 @@ def accumulate_add(srcs, dst, valid: Optional[Tuple[int, int]] = None,
     dt = _torch_dtype_code(dst)
     rows, cols, ld = _check_group(list(srcs) + [dst], dst, "tensor")
     vr, vc = (rows, cols) if valid is None else valid
+    if vr == 0 or vc == 0:
+        return
     handle = _stream_handle(stream, dst.device)
     with torch.cuda.device(dst.device):
         _raise_on(ptored_accumulate_add([s.data_ptr() for s in srcs], len(srcs), dst.data_ptr(),

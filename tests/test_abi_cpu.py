@@ -349,6 +349,8 @@ def test_tensor_wrappers_reject_bad_groups():
     with pytest.raises(ValueError):  # CPU tensors are not on a GPU
         crc.allreduce([a, torch.zeros(4, 8)])
     assert crc.ring_bounds(100, 4, "bf16") == [0, 32, 64, 80, 100]
+    with pytest.raises(ValueError):  # an op the library does not have
+        crc.treduce([a, a], torch.zeros(4, 8), op="mean")
 
 
 def test_c_consumer_program_compiles(tmp_path):

@@ -460,6 +460,20 @@ def test_tensor_wrappers_of_the_collectives():
                                op="sum")
     for d, w_ in zip(dsts, want):
         assert np.array_equal(d.cpu().numpy(), w_)
+
+    # empty tensors (no storage): nothing to reduce, no error, nothing launched
+    e = [torch.empty(0, 8, device="cuda") for _ in range(3)]
+    crc.treduce(e[:2], e[2])
+    crc.allreduce(e)
+    crc.accumulate_add(e[:2], e[2])
+    crc.reduce_scatter_ring([torch.empty(0, device="cuda")] * 2,
+                            [torch.empty(0, device="cuda")] * 2)
+    # a zero-width valid rectangle on real tensors writes nothing
+    a = torch.ones(4, 8, device="cuda")
+    d = torch.full((4, 8), 7.0, device="cuda")
+    crc.treduce([a, a], d, valid=(4, 0))
+    torch.cuda.synchronize()
+    assert bool((d == 7.0).all())
     assert crc.ring_bounds(count, n, torch.int32) == list(oracle.ring_bounds(count, n, "i32"))
 
     srcs = [torch.from_numpy(rng.integers(-2 ** 20, 2 ** 20, (rows, cols), dtype=np.int32))
