@@ -196,7 +196,9 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         const uint64_t streams = p.family == kFamCopy ? 2u
                                  : mode == kModeAllreduce ? 2u * (uint64_t)nranks
                                                           : (uint64_t)nranks + 1u;
-        p.wgs_per_cu = wgs_per_cu_for(streams * slot_bytes, mode == kModeAllreduce);
+        const bool runtime_loop =
+            p.family == kFamVecRuntime && (!p.lds_stages || nranks > 16);
+        p.wgs_per_cu = wgs_per_cu_for(streams * slot_bytes, mode == kModeAllreduce, runtime_loop);
     }
     const int64_t vec = p.vec_elems;
     if (p.rows_mode) {
@@ -208,8 +210,7 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         // few workgroups resident per CU they measured 3-4% faster than the
         // flattened walk on ragged rows.
         p.rows_mode = kWalkFlat;
-        if (p.family != kFamElem && mode != kModeAccumulate && !p.lds_stages &&
-            (flags & PTORED_FLAT_WALK) == 0) {
+        if (p.family != kFamElem && mode != kModeAccumulate && (flags & PTORED_FLAT_WALK) == 0) {
             const int64_t numbered = (p.lead + valid_cols * p.esize) / 16;
             const int64_t full = numbered - (p.lead + 15) / 16;
             const int64_t per_tile = (int64_t)kBlock * p.unroll;
@@ -727,7 +728,8 @@ extern "C" int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, v
         if (st != PTORED_OK) return st;
         if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages) {
             if (p.wgs_per_cu > 0)  // the ring kernel moves one slot per thread
-                p.wgs_per_cu = wgs_per_cu_for((uint64_t)(nranks + 1) * kBlock * 16u, false);
+                p.wgs_per_cu = wgs_per_cu_for((uint64_t)(nranks + 1) * kBlock * 16u, false,
+                                              p.family == kFamVecRuntime);
             return run_ring(p, srcs, dsts, bounds, count, stream);
         }
     }

@@ -566,16 +566,17 @@ __device__ __forceinline__ void fold_slots(SrcFn src, uint32_t n, const uint32_t
     }
 }
 
-// One main tile: U full 16-byte slots per thread, NR sources.  Row tiles:
-// tile t is column chunk c of row r (t = r * tiles_per_row + c, split on
-// the scalar unit), so every wave's 1 KiB run starts a whole number of KiB
-// past the row's slot origin and never shares a cache line with another
-// wave; the other walks number the slots straight through.
-template <int DT, int OP, int NR, int U, int WALK, bool ALL>
-__device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
+// Byte offsets of the U slots a lane folds in main tile t (kOutOfRange for
+// slots past a row's end or before its first full slot).  Row tiles: tile t
+// is column chunk c of row r (t = r * tiles_per_row + c, split on the scalar
+// unit), so every wave's 1 KiB run starts a whole number of KiB past the
+// row's slot origin and never shares a cache line with another wave; the
+// other walks number the slots straight through.
+template <int U, int WALK>
+__device__ __forceinline__ void main_tile_offsets(const KArgs& a, uint32_t t,
+                                                  uint32_t (&off)[U]) {
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t in_tile = wave * (uint32_t)(64 * U) + lane;
-    uint32_t off[U];
     if constexpr (WALK == kWalkRowTiles) {
         const uint32_t row = fast_div(t, a.div_tiles);
         const uint32_t v0 = (t - row * a.tiles_per_row) * (uint32_t)(kBlock * U) + in_tile;
@@ -590,6 +591,13 @@ __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
 #pragma unroll
         for (int u = 0; u < U; ++u) off[u] = slot_offset<WALK>(a, base + (uint32_t)(u * 64));
     }
+}
+
+// One main tile: U full 16-byte slots per thread, NR sources.
+template <int DT, int OP, int NR, int U, int WALK, bool ALL>
+__device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
+    uint32_t off[U];
+    main_tile_offsets<U, WALK>(a, t, off);
     const rsrc_t rd = make_rsrc(a.dst, a.extent);
     u32x4 out[U];
     fold_slots<DT, OP, NR, U>([&](uint32_t k) { return make_rsrc(a.src[k], a.extent); },
@@ -651,7 +659,9 @@ struct LdsStages {
 template <int DT, int OP, int S, int WALK>
 __device__ __forceinline__ void main_tile_lds(const KArgs& a, uint32_t t, LdsStages<S>& st) {
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const uint32_t off = slot_offset<WALK>(a, t * (uint32_t)kBlock + wave * 64u + lane);
+    uint32_t offs[1];
+    main_tile_offsets<1, WALK>(a, t, offs);
+    const uint32_t off = offs[0];
     const uint32_t n = a.nranks;
     // prologue: the first min(S, N) ranks
 #pragma unroll
@@ -856,7 +866,8 @@ __global__ __launch_bounds__(kBlock) void treduce_kernel(const KArgs a) {
 }
 
 // The LDS ping-pong kernel: main tiles through LDS stages (one slot per
-// thread), row remainders (first) as in treduce_kernel.  Runtime rank count.
+// thread, any walk), tail tiles (first) as in treduce_kernel.  Runtime rank
+// count.
 template <int DT, int OP, int ES, int WALK, int S>
 __global__ __launch_bounds__(kBlock) void treduce_lds_kernel(const KArgs a) {
     __shared__ LdsStages<S> stages;

@@ -102,10 +102,13 @@ static int dispatch_op(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
         default: return kLaunchNoKernel;
         }
     }
-    if (p.lds_stages) {  // LDS ping-pong variant: contiguous or flattened walks
+    if (p.lds_stages) {  // LDS ping-pong variant
         switch (p.rows_mode) {
         case kWalkContig:
             return launch<treduce_lds_kernel<DT, OP, ES, kWalkContig, kLdsStages>>(p, a, cu, s);
+        case kWalkRowTiles:
+            return launch<treduce_lds_kernel<DT, OP, ES, kWalkRowTiles, kLdsStages>>(p, a, cu,
+                                                                                   s);
         case kWalkFlat:
             return launch<treduce_lds_kernel<DT, OP, ES, kWalkFlat, kLdsStages>>(p, a, cu, s);
         default: return kLaunchNoKernel;

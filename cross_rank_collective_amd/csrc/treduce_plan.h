@@ -157,7 +157,12 @@ constexpr int kElemUnroll = 4;     // elements per thread, element-wise path
 // four element types and every walk: about 64-136 KiB in flight per CU for
 // the reduction and the ring, fewer for the in-place allreduce, whose
 // stores are half of its bytes (64-96 KiB).
-constexpr int wgs_per_cu_for(uint64_t tile_bytes, bool allreduce) {
+// The runtime rank loop keeps only one group of four ranks' loads in
+// flight per wave, so it wants more waves than its tile bytes suggest: 10
+// per CU (6 for the allreduce) measured best at N = 17-32 for bf16 Sum
+// (whose per-step rounding chain needs the most waves), f16 and i32.
+constexpr int wgs_per_cu_for(uint64_t tile_bytes, bool allreduce, bool runtime_loop) {
+    if (runtime_loop) return allreduce ? 6 : 10;
     if (allreduce)
         return tile_bytes <= 8u * 1024u ? 8 : (tile_bytes <= 16u * 1024u ? 5 : 3);
     return tile_bytes <= 5u * 1024u    ? 16
@@ -174,7 +179,7 @@ constexpr int kLdsUnitsPerCu = 128;
 // A launch needs this many waves of capped workgroups to be worth capping.
 constexpr int kCapMinRounds = 4;
 constexpr int kLdsStages = 4;      // LDS stages per wave in the ping-pong variant
-constexpr int kRuntimeUnroll = 2;  // slots per thread, runtime rank count
+constexpr int kRuntimeUnroll = 1;  // slots per thread, runtime rank count
 
 // Launch one kernel of the plan's family on `a`, on a persistent grid sized
 // for `cu_count` compute units.

@@ -132,8 +132,9 @@ def test_plan_paths():
 def test_plan_resident_workgroups():
     """Workgroups (one wave each) kept resident per CU by one-tile-per-block
     launches, from the bytes one tile moves (1 KiB per stream per slot row):
-    16 up to 5 KiB, 12 up to 7, 10 up to 13, 8 up to 17, 4 beyond; no limit
-    for the element-wise kernel, persistent grids or on request."""
+    16 up to 5 KiB, 12 up to 7, 10 up to 13, 8 up to 17; 10 for the runtime
+    rank loop; no limit for the element-wise kernel, persistent grids or on
+    request."""
     assert _plan(n=16, srcs=A[:16], dtype=3).wgs_per_cu == 8   # 17 x 1 KiB
     assert _plan(n=8, srcs=A[:8], dtype=1).wgs_per_cu == 10    # 9 x 1 KiB
     assert _plan(n=12, srcs=A[:12]).wgs_per_cu == 10           # 13 x 1 KiB
@@ -142,7 +143,9 @@ def test_plan_resident_workgroups():
     assert _plan(n=4, srcs=A[:4]).wgs_per_cu == 16             # 5 x 1 KiB
     assert _plan(n=2, srcs=A[:2]).wgs_per_cu == 12             # 3 x 2 KiB (2 slots per thread)
     assert _plan(n=1).wgs_per_cu == 16                         # copy: 2 x 2 KiB
-    assert _plan(n=17, srcs=A[:17]).wgs_per_cu == 4            # 18 x 2 KiB
+    assert _plan(n=17, srcs=A[:17]).wgs_per_cu == 10           # runtime rank loop
+    info = _plan(n=64, srcs=A[:64])
+    assert (info.wgs_per_cu, info.slots_per_thread) == (10, 1)
     assert _plan(srcs=[A[0], A[1] + 4]).wgs_per_cu == 0        # element-wise
     assert _plan(tuning=B.tuning(flags=B.PTORED_FULL_OCCUPANCY)).wgs_per_cu == 0
     assert _plan(tuning=B.tuning(blocks_per_cu=2)).wgs_per_cu == 0
@@ -236,9 +239,12 @@ def test_plan_walk_and_slots():
     # 8 or more chunks per row: row tiles whatever the last chunk holds
     info = _plan(n=4, srcs=A[:4], rows=4, cols=4 * 7 * 64 + 4, ld=1800, vr=4, vc=1796)
     assert info.rows_mode == 1
-    # the LDS variant walks flattened
+    # the LDS variant takes the same walks
     lds = B.tuning(flags=B.PTORED_LDS_PINGPONG)
     info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000, tuning=lds)
+    assert info.rows_mode == 1
+    info = _plan(n=4, srcs=A[:4], rows=64, cols=1000, ld=1024, vr=60, vc=1000,
+                 tuning=B.tuning(flags=B.PTORED_LDS_PINGPONG | B.PTORED_FLAT_WALK))
     assert info.rows_mode == 2
     info = _plan(rows=1, cols=13, ld=16, vr=1, vc=13, dtype=2)  # one row: contiguous f16
     assert (info.rows_mode, info.vec_elems, info.slots) == (0, 8, 2)
