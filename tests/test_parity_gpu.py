@@ -245,14 +245,15 @@ SPILL_SHAPES = [
 def test_row_tiles_with_spill_slots(dtype):
     """Row tiles whose rows end a few slots past their last whole tile: those
     slots folded in the tail tiles, one per lane across rows.  Reduction and
-    allreduce, unrolled, two-slot (N <= 2) and runtime rank loops."""
+    allreduce, unrolled, two-slot (N <= 2) and runtime rank loops, and the
+    LDS ping-pong variant."""
     rng = np.random.default_rng({"f32": 81, "bf16": 82, "f16": 83, "i32": 84}[dtype])
     es = ESIZE[dtype]
     for case, (rows, cols, ld, vr, vc, off) in enumerate(SPILL_SHAPES):
         if vc > cols:
             continue
         for n, flags in ((2, 0), (5, B.PTORED_ROW_TILES | B.PTORED_FORCE_ROWS),
-                         (17, B.PTORED_FORCE_ROWS)):
+                         (17, B.PTORED_FORCE_ROWS), (6, B.PTORED_LDS_PINGPONG)):
             if rows * ld * n > 30_000_000:
                 continue
             root = int(rng.integers(0, n))
