@@ -131,16 +131,26 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
     p.rows_mode = contiguous ? 0 : 1;
     p.total_elems = contiguous ? (valid_rows == 1 ? valid_cols : valid_rows * ld) : 0;
 
-    // The 16-byte vector path needs every buffer to start at the same byte
-    // offset within a 16-byte block, every row start to keep it (pitch a
-    // multiple of 16 bytes), and every valid row (or the span) to reach the
-    // end of the block it starts in, so that its head is exactly the rest
-    // of that block.  Slots are numbered from the coarsest boundary at which
-    // every buffer (and row) has the same offset: 1 KiB, so that each wave's
-    // 1 KiB run is one aligned KiB (measured 3-4% faster than runs at 128-512
-    // bytes past it), else a 128-byte line, so that it covers 8 whole lines
-    // (12% faster than runs straddling lines), else 16 bytes.  `lead` is the
-    // offset from that origin.
+    // The 16-byte vector path numbers slots from an origin shared by every
+    // buffer (byte offsets are taken from each buffer's own base, so slot k
+    // holds the same elements everywhere); `lead` is the offset of element 0
+    // past that origin, and a row or span starting inside a 16-byte block
+    // begins with a head of element-wise items.  When every buffer starts at
+    // the same offset within a 16-byte block and every row start keeps it
+    // (pitch a multiple of 16 bytes), slots are numbered from the coarsest
+    // boundary at which every buffer (and row) has the same offset: 1 KiB, so
+    // that each wave's 1 KiB run is one aligned KiB (measured 3-4% faster than
+    // runs at 128-512 bytes past it), else a 128-byte line, so that it covers 8
+    // whole lines (12% faster than runs straddling lines), else 16 bytes.
+    // Otherwise the slots keep one buffer aligned and the others take
+    // unaligned 16-byte accesses, which gfx9 and later serve in the unaligned
+    // access mode the HSA ABI enables: buffers at different offsets take the
+    // last pointer's alignment (dst for the reduction); rows whose pitch is
+    // not a multiple of 16 bytes number their slots from each row's start.
+    // Measured on MI355X against one element per slot: +14-23% for 2-byte
+    // types and odd pitches, level for 4-byte types at N = 16.  Push-with-add
+    // (whose atomics need naturally aligned words) and the LDS variant (whose
+    // loads go straight to LDS) keep the shared-offset rule.
     bool use_vec = (flags & PTORED_FORCE_ELEMENTWISE) == 0;
     auto common_offset = [&](uintptr_t align) {
         const uintptr_t off = reinterpret_cast<uintptr_t>(ptrs[0]) & (align - 1u);
@@ -149,18 +159,34 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         if (p.rows_mode && ((ld * p.esize) & (int64_t)(align - 1u)) != 0) return -1;
         return (int)off;
     };
+    // offset of the last pointer past an `align` boundary, if every row keeps it
+    auto anchor_offset = [&](uintptr_t align) {
+        if (p.rows_mode && ((ld * p.esize) & (int64_t)(align - 1u)) != 0) return -1;
+        return (int)(reinterpret_cast<uintptr_t>(ptrs[nptrs - 1]) & (align - 1u));
+    };
+    const bool lds = (flags & PTORED_LDS_PINGPONG) != 0 && mode == kModeReduce && nranks > 1;
+    const bool unaligned_ok = mode != kModeAccumulate && !lds;
     int lead = use_vec ? common_offset(16) : -1;
-    if (lead < 0) {
-        use_vec = false;
-    } else {
-        const int64_t row_bytes = (contiguous ? p.total_elems : valid_cols) * p.esize;
-        if (lead % 16 != 0 && lead % 16 + row_bytes < 16) use_vec = false;
+    if (lead >= 0) {
         const int kib = common_offset(1024), line = common_offset(128);
         if (kib >= 0) {
             lead = kib;
         } else if (line >= 0) {
             lead = line;
         }
+    } else if (use_vec && unaligned_ok) {
+        if (p.rows_mode && ((ld * p.esize) & 15) != 0) {
+            lead = 0;  // slots from each row's start
+        } else {
+            const int kib = anchor_offset(1024), line = anchor_offset(128);
+            lead = kib >= 0 ? kib : (line >= 0 ? line : anchor_offset(16));
+        }
+    } else {
+        use_vec = false;
+    }
+    if (use_vec) {
+        const int64_t row_bytes = (contiguous ? p.total_elems : valid_cols) * p.esize;
+        if (lead % 16 != 0 && lead % 16 + row_bytes < 16) use_vec = false;
     }
     p.lead = use_vec ? lead : 0;
 

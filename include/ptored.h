@@ -108,13 +108,18 @@ typedef enum ptored_status {
  * UNSUPPORTED (dtype or op outside the enums), INVALID_ARG (a pointer not
  * aligned to the element size), OVERLAP.  ERR_HIP is returned when the
  * launch fails.  Pointers or row pitches that are not 16-byte aligned are
- * not errors.  When every buffer starts at the same offset within a 16-byte
- * block, the pitch is a multiple of 16 bytes and every valid row reaches the
- * next 16-byte boundary, the 16-byte vector kernels still run (each row's
- * bytes before that boundary folded as a head); otherwise misaligned data
- * selects an element-wise kernel.  Buffers that also share their offset
- * within 1 KiB (or a 128-byte line) are walked in aligned 1 KiB runs (or
- * whole lines) whatever that offset.
+ * not errors: the 16-byte vector kernels run on any alignment.  When every
+ * buffer starts at the same offset within a 16-byte block and the pitch is
+ * a multiple of 16 bytes, every access is aligned (each row's bytes before
+ * the next 16-byte boundary folded as a head), and buffers that also share
+ * their offset within 1 KiB (or a 128-byte line) are walked in aligned 1 KiB
+ * runs (or whole lines) whatever that offset.  Buffers at different offsets
+ * keep dst aligned the same way and read the sources with unaligned 16-byte
+ * loads; a pitch that is not a multiple of 16 bytes numbers each row's
+ * slots from the row's start, every access unaligned.  A valid row (or
+ * span) that does not reach the 16-byte boundary it starts before, the
+ * PTORED_LDS_PINGPONG variant on misaligned data and PTORED_FORCE_ELEMENTWISE
+ * take an element-wise kernel.
  */
 int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int64_t rows,
                    int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
@@ -164,7 +169,9 @@ int ptored_treduce_ex(const void* const* srcs, int nranks, int root, void* dst, 
 #define PTORED_PATH_COPY 1        /* N == 1 copy */
 #define PTORED_PATH_VEC_FIXED 2   /* 16-B vectors, N unrolled at compile time */
 #define PTORED_PATH_VEC_RUNTIME 3 /* 16-B vectors, rank-count loop */
-#define PTORED_PATH_ELEMENTWISE 4 /* one element per slot (misaligned data) */
+#define PTORED_PATH_ELEMENTWISE 4 /* one element per slot (forced, rows shorter than their
+                                     first 16-byte block, or misaligned data through the LDS
+                                     variant or push-with-add) */
 
 typedef struct ptored_plan_info {
     int32_t path;          /* PTORED_PATH_* */
@@ -178,8 +185,10 @@ typedef struct ptored_plan_info {
     int32_t lead;          /* vector path: bytes past the slot origin at which every buffer
                               starts -- the coarsest of a 1 KiB, 128-byte or 16-byte
                               boundary at which every buffer (and, for rows, the pitch)
-                              has the same offset; a row starting inside a 16-byte block
-                              begins with a head */
+                              has the same offset; with none, dst's offset past the
+                              coarsest such boundary the pitch keeps, or 0 (slots from
+                              each row's start) for a pitch off the 16-byte grid; a row
+                              starting inside a 16-byte block begins with a head */
 } ptored_plan_info;
 
 /* Validate like ptored_treduce_ex and describe the launch it would make,
@@ -228,12 +237,13 @@ int ptored_ring_bounds(int64_t count, int nranks, int dtype, int64_t* bounds);
  *             elements.  dsts[s] may be srcs[s] (in place into the owner's
  *             window), any other source or another dst; partial overlaps are
  *             rejected.
- * Errors as ptored_treduce_ex.  When every source and dst starts at the same
- * offset within a 16-byte block, one launch covers every segment (a window of at most
- * max_launch_bytes per launch): each workgroup takes one segment's tile and
- * folds it in that segment's ring order, and one more tile per segment
- * folds its elements outside whole 16-byte slots.  Otherwise, or with
- * PTORED_SEGMENT_LAUNCHES, one launch per non-empty segment.
+ * Errors as ptored_treduce_ex.  When the 16-byte kernels apply (at any
+ * alignment, as for ptored_treduce), one launch covers every segment (a
+ * window of at most max_launch_bytes per launch): each workgroup takes one
+ * segment's tile and folds it in that segment's ring order, and one more
+ * tile per segment folds its elements outside whole 16-byte slots.
+ * Otherwise, or with PTORED_SEGMENT_LAUNCHES, one launch per non-empty
+ * segment.
  */
 int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, void* const* dsts,
                                int64_t count, int dtype, int op, const ptored_tuning* tuning,
@@ -249,7 +259,10 @@ int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, void* const*
  * exact).  A 16-bit element that does not fill its aligned 32-bit word is
  * added by a compare-and-swap on that word which rewrites only its own half.
  * dst must be device memory of this GPU and must not overlap any source
- * (not even exactly).  Other arguments and errors as ptored_treduce_ex.
+ * (not even exactly).  The 16-byte kernel needs every buffer at one offset
+ * within a 16-byte block and a pitch on the 16-byte grid (its atomics take
+ * naturally aligned words); otherwise sources are added element by
+ * element.  Other arguments and errors as ptored_treduce_ex.
  */
 int ptored_accumulate_add(const void* const* srcs, int nranks, void* dst, int64_t rows,
                           int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,

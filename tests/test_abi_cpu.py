@@ -114,10 +114,16 @@ def test_plan_paths():
     assert B.PATHS[_plan(n=16, srcs=A[:16]).path] == "vec_fixed"
     assert B.PATHS[_plan(n=17, srcs=A[:17]).path] == "vec_runtime"
     assert B.PATHS[_plan(n=64, srcs=A[:64]).path] == "vec_runtime"
-    # a misaligned source pointer or row pitch selects the element-wise kernel
-    assert B.PATHS[_plan(srcs=[A[0], A[1] + 4]).path] == "elementwise"
-    assert B.PATHS[_plan(dst=D + 2, dtype=2).path] == "elementwise"
-    assert B.PATHS[_plan(rows=4, cols=3, ld=5, vr=4, vc=3).path] == "elementwise"
+    # buffers at different offsets within 16 bytes, or a row pitch off the
+    # 16-byte grid, keep the vector path with unaligned accesses ...
+    assert B.PATHS[_plan(srcs=[A[0], A[1] + 4]).path] == "vec_fixed"
+    assert B.PATHS[_plan(dst=D + 2, dtype=2).path] == "vec_fixed"
+    assert B.PATHS[_plan(rows=4, cols=3, ld=5, vr=4, vc=3).path] == "vec_fixed"
+    # ... except through the LDS variant, which keeps the shared-offset rule
+    t = B.tuning(flags=B.PTORED_LDS_PINGPONG)
+    assert B.PATHS[_plan(n=5, srcs=A[:4] + [A[4] + 4], tuning=t).path] == "elementwise"
+    assert B.PATHS[_plan(n=5, srcs=A[:5], tuning=t, rows=4, cols=3, ld=5, vr=4,
+                         vc=3).path] == "elementwise"
     # forcing flags
     t = B.tuning(flags=B.PTORED_FORCE_ELEMENTWISE)
     assert B.PATHS[_plan(tuning=t).path] == "elementwise"
@@ -146,7 +152,9 @@ def test_plan_resident_workgroups():
     assert _plan(n=17, srcs=A[:17]).wgs_per_cu == 10           # runtime rank loop
     info = _plan(n=64, srcs=A[:64])
     assert (info.wgs_per_cu, info.slots_per_thread) == (10, 1)
-    assert _plan(srcs=[A[0], A[1] + 4]).wgs_per_cu == 0        # element-wise
+    assert _plan(srcs=[A[0], A[1] + 4]).wgs_per_cu == 12       # unaligned: same rule
+    t = B.tuning(flags=B.PTORED_FORCE_ELEMENTWISE)
+    assert _plan(tuning=t).wgs_per_cu == 0                     # element-wise
     assert _plan(tuning=B.tuning(flags=B.PTORED_FULL_OCCUPANCY)).wgs_per_cu == 0
     assert _plan(tuning=B.tuning(blocks_per_cu=2)).wgs_per_cu == 0
     assert _plan(vr=0).wgs_per_cu == 0
@@ -154,20 +162,26 @@ def test_plan_resident_workgroups():
 
 def test_plan_common_lead():
     """Buffers that all start the same number of bytes past a 16-byte boundary
-    keep the vector path (rows begin with a head); a different offset, a
-    pitch off the 16-byte grid, or a row too short to reach the boundary
-    select the element-wise kernel."""
+    keep the vector path (rows begin with a head); buffers at different
+    offsets take dst's alignment (the sources are read unaligned), a pitch
+    off the 16-byte grid numbers each row's slots from its start, and a row
+    too short to reach the boundary selects the element-wise kernel."""
     co = [A[0] + 4, A[1] + 4]
     info = _plan(srcs=co, dst=D + 4)                               # 16 contiguous f32
     assert (B.PATHS[info.path], info.lead, info.launches) == ("vec_fixed", 4, 1)
     info = _plan(srcs=co, dst=D + 8)                               # dst at another offset
-    assert (B.PATHS[info.path], info.lead) == ("elementwise", 0)
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 8)
+    info = _plan(srcs=co, dst=D + 520)                             # dst's 1 KiB offset
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 520)
     info = _plan(srcs=[A[0] + 6, A[1] + 6], dst=D + 6, dtype=2, rows=8, cols=10, ld=16,
                  vr=7, vc=9)                                       # f16 rows of 32 B pitch
     assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 6)
+    info = _plan(srcs=[A[0] + 6, A[1] + 10], dst=D + 2, dtype=2, rows=8, cols=10, ld=16,
+                 vr=7, vc=9)                                       # dst's offset, 32 B pitch
+    assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 2)
     info = _plan(srcs=[A[0] + 6, A[1] + 6], dst=D + 6, dtype=2, rows=8, cols=10, ld=12,
-                 vr=7, vc=9)                                       # 24 B pitch
-    assert B.PATHS[info.path] == "elementwise"
+                 vr=7, vc=9)                                       # 24 B pitch: row starts
+    assert (B.PATHS[info.path], info.rows_mode != 0, info.lead) == ("vec_fixed", True, 0)
     info = _plan(srcs=[A[0] + 12, A[1] + 12], dst=D + 12, rows=1, cols=1, ld=1, vr=1, vc=1)
     assert (B.PATHS[info.path], info.lead) == ("vec_fixed", 12)   # exactly [12, 16)
     info = _plan(srcs=[A[0] + 8, A[1] + 8], dst=D + 8, rows=1, cols=1, ld=1, vr=1, vc=1)

@@ -191,8 +191,8 @@ def test_allreduce_full_size_workload():
 
 # Launch variants of the reduce-scatter: (label, flags, blocks_per_cu,
 # max_launch_bytes, misaligned dst 0).  The default takes one launch over
-# every segment when all streams are 16-byte aligned; the misaligned case
-# and PTORED_SEGMENT_LAUNCHES take one launch per segment.
+# every segment, the misaligned case included (its other streams are read
+# and written unaligned); PTORED_SEGMENT_LAUNCHES takes one per segment.
 RING_VARIANTS = [
     ("single", 0, 0, 0, False),
     ("elementwise", B.PTORED_FORCE_ELEMENTWISE, 0, 0, False),

@@ -124,7 +124,8 @@ def test_random_small_cases(dtype):
 
 
 # Shapes for buffers that all start `lead` bytes past a 16-byte boundary
-# (pitches are multiples of 16 bytes for every element size).
+# (2-D pitches are multiples of 16 bytes for every element size; the spans'
+# pitches are not, which matters when the row walk is forced).
 LEAD_SHAPES = [
     # rows, cols, ld, valid_rows, valid_cols
     (1, 5003, 5003, 1, 5003),      # one contiguous span
@@ -171,8 +172,13 @@ def test_common_lead_keeps_vector_path(dtype):
             contig = (vc == ld or vr == 1) and not flags & B.PTORED_FORCE_ROWS
             row_bytes = ((vc if vr == 1 else vr * ld) if contig else vc) * es
             # else the element-wise kernel: a row that never reaches the
-            # boundary, or 2-D rows whose pitch is off the 16-byte grid
-            vector = lead + row_bytes >= 16 and (contig or (ld * es) % 16 == 0)
+            # boundary; rows whose pitch is off the 16-byte grid number their
+            # slots from each row's start (element-wise only through the LDS
+            # variant, which keeps the shared-offset rule)
+            if contig or (ld * es) % 16 == 0:
+                vector = lead + row_bytes >= 16
+            else:
+                vector = not (flags & B.PTORED_LDS_PINGPONG and n > 1)
             assert (B.PATHS[info.path] != "elementwise") == vector, label
             dst, st, bufs = run_gpu(srcs, dtype, op, root, rows, cols, ld, vr, vc, offsets=offs,
                                     dst_offset=dst_off, tuning=t, alias=alias, label=label)
@@ -218,8 +224,11 @@ def test_common_line_offset(dtype):
             assert st_plan == 0
             contig = (vc == ld or vr == 1) and not flags & B.PTORED_FORCE_ROWS
             if B.PATHS[info.path] != "elementwise":
-                origin = next(a for a in (1024, 128, 16) if contig or (ld * es) % a == 0)
-                assert info.lead == off % origin, label
+                if contig or (ld * es) % 16 == 0:
+                    origin = next(a for a in (1024, 128, 16) if contig or (ld * es) % a == 0)
+                    assert info.lead == off % origin, label
+                else:
+                    assert info.lead == 0, label  # slots from each row's start
             dst, st, bufs = run_gpu(srcs, dtype, op, root, rows, cols, ld, vr, vc,
                                     offsets=[off] * n, dst_offset=off, tuning=t, alias=alias,
                                     label=label)
@@ -239,6 +248,73 @@ SPILL_SHAPES = [
     (61, 12288, 12288, 61, 12287, 64),  # the ragged f16 shape at a 64-byte offset
     (5, 300, 320, 5, 260, 36),        # a head, whole tiles, spill and a remainder
 ]
+
+
+# Shapes for the unaligned vector path: buffers at different offsets within
+# 16 bytes, and row pitches off the 16-byte grid (the last two).
+UNALIGNED_SHAPES = [
+    # rows, cols, ld, valid_rows, valid_cols
+    (1, 70001, 70001, 1, 70001),   # one contiguous span
+    (41, 1040, 1040, 41, 1040),    # rows back to back: contiguous
+    (37, 1024, 1040, 35, 1021),    # 2-D, pitch on the 16-byte grid, ragged row ends
+    (9, 4100, 4112, 9, 4099),      # row tiles: 4+ chunks per row
+    (37, 1030, 1031, 35, 1029),    # odd pitch: each row at its own offset
+    (12, 4099, 4101, 12, 4099),    # odd pitch, full rows
+]
+
+
+@pytest.mark.parametrize("dtype", DT)
+def test_unaligned_vector_path(dtype):
+    """Buffers at different offsets within 16 bytes take the vector kernels
+    with dst's alignment (the other buffers read unaligned), and odd row
+    pitches number each row's slots from its start; against the oracle in
+    every walk, with windows, the runtime rank loop and in place.  The plan
+    is checked to be the vector path, except through the LDS variant."""
+    rng = np.random.default_rng({"f32": 181, "bf16": 182, "f16": 183, "i32": 184}[dtype])
+    es = ESIZE[dtype]
+    variants = [("auto", 0, 0), ("flat", B.PTORED_FORCE_ROWS | B.PTORED_FLAT_WALK, 0),
+                ("row_tiles", B.PTORED_FORCE_ROWS | B.PTORED_ROW_TILES, 0),
+                ("runtime_n", B.PTORED_FORCE_RUNTIME_N, 0), ("windows", 0, 1008),
+                ("windows_rows", B.PTORED_FORCE_ROWS, 4096 + 48), ("lds", B.PTORED_LDS_PINGPONG, 0)]
+    case = 0
+    for rows, cols, ld, vr, vc in UNALIGNED_SHAPES:
+        for vname, flags, mlb in variants:
+            n = int(rng.choice([1, 2, 3, 8, 16, 20]))
+            root = int(rng.integers(0, n))
+            op = OPS[case % 4]
+            offs = [es * int(rng.integers(0, 16 // es)) + 16 * int(rng.integers(0, 4))
+                    for _ in range(n)]
+            if len({o % 16 for o in offs}) == 1 and n > 1:
+                offs[-1] = (offs[-1] + es) % 64  # at least two offsets within 16 bytes
+            dst_off = es * int(rng.integers(0, 1024 // es))
+            alias = int(rng.integers(0, n)) if case % 6 == 5 else -1
+            size = (rows - 1) * ld + cols
+            srcs = [_rand_elems(dtype, rng, size) for _ in range(n)]
+            t = B.tuning(flags=flags, max_launch_bytes=mlb)
+            label = (f"unaligned#{case} {vname} {rows}x{cols} ld={ld} valid={vr}x{vc} N={n} "
+                     f"offs={offs[:4]} dst={dst_off if alias < 0 else offs[alias]}")
+            d_off = offs[alias] if alias >= 0 else dst_off
+            st_plan, info = B.ptored_treduce_plan(
+                [0x1000000 + o for o in offs], n, root, 0x9000000 + d_off, rows, cols, ld, vr,
+                vc, B.DTYPES[dtype], B.OPS[op], t)
+            assert st_plan == 0
+            contig = (vc == ld or vr == 1) and not flags & B.PTORED_FORCE_ROWS
+            shared = len({o % 16 for o in offs + [d_off]}) == 1 and (contig or (ld * es) % 16 == 0)
+            if flags & B.PTORED_LDS_PINGPONG and not shared and n > 1:
+                assert B.PATHS[info.path] == "elementwise", label
+            else:
+                assert B.PATHS[info.path] != "elementwise", label
+                if not shared and (contig or (ld * es) % 16 == 0):
+                    origin = next(a for a in (1024, 128, 16) if contig or (ld * es) % a == 0)
+                    assert info.lead == d_off % origin, label
+                elif not shared:
+                    assert info.lead == 0, label  # slots from each row's start
+            dst, st, bufs = run_gpu(srcs, dtype, op, root, rows, cols, ld, vr, vc, offsets=offs,
+                                    dst_offset=dst_off, tuning=t, alias=alias, label=label)
+            assert st == 0, B.ptored_status_string(st)
+            _check(srcs, dtype, op, root, rows, cols, ld, vr, vc, dst, bufs, alias=alias,
+                   label=label)
+            case += 1
 
 
 @pytest.mark.parametrize("dtype", DT)
