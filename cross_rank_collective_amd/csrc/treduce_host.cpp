@@ -510,7 +510,9 @@ int run(const Plan& plan, const char* const* ordered, void* dst, hipStream_t str
     a.nranks = (uint32_t)p.nranks;
     a.xcd_remap = p.xcd_remap ? 1u : 0u;
     // Vector path: address every buffer from its slot origin, `lead` bytes
-    // before the data (a 1 KiB, 128-byte or 16-byte boundary).
+    // before the data (a 1 KiB, 128-byte or 16-byte boundary of every buffer,
+    // or of dst alone when the buffers share no offset; for a pitch off the
+    // 16-byte grid, lead is 0 and each row's slots start at the row).
     const char* base[PTORED_MAX_RANKS];
     for (int r = 0; r < p.nranks; ++r) base[r] = ordered[r] - p.lead;
     char* d = static_cast<char*>(dst) - p.lead;
@@ -581,9 +583,10 @@ int launch_ring(const Plan& p, const RingArgs& a, int cu, hipStream_t s) {
 }
 
 // The ring reduce-scatter in one launch per window of max_launch_bytes (one
-// launch in all for streams up to 2 GiB).  Every stream starts at the same
-// offset within a 16-byte block, so windows counted from that block's start
-// in multiples of 16 keep whole slots whole.
+// launch in all for streams up to 2 GiB).  Windows are counted from `lead`
+// bytes before every stream's start in multiples of 16, so whole slots stay
+// whole (aligned when the streams share their offset within a 16-byte block,
+// else on the last dst's alignment, the others accessed unaligned).
 // `bounds` are the segment boundaries in elements.
 int run_ring(const Plan& plan, const void* const* srcs, void* const* dsts, const int64_t* bounds,
              int64_t count, hipStream_t stream) {
@@ -593,8 +596,9 @@ int run_ring(const Plan& plan, const void* const* srcs, void* const* dsts, const
     const Plan p = with_device(plan, f);
     const int cu = f.cu;
     const int n = p.nranks;
-    // Streams that all start `lead` bytes past a 16-byte boundary are
-    // addressed from that boundary; segment bounds move by the same bytes.
+    // Every stream is addressed from `lead` bytes before its start (a 16-byte
+    // boundary of every stream, or of the last dst); segment bounds move by
+    // the same bytes.
     const int64_t es = p.esize, lead = p.lead, total = lead + count * es;
     RingArgs a{};
     a.nranks = (uint32_t)n;
@@ -747,7 +751,8 @@ extern "C" int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, v
     ring_bounds(count, nranks, dtype, bounds);
     const uint32_t flags = tuning ? tuning->flags : 0u;
     if (nranks >= 2 && count > 0 && (flags & PTORED_SEGMENT_LAUNCHES) == 0) {
-        // One launch over every segment when all 2N streams take 16-byte slots.
+        // One launch over every segment when the 2N streams take 16-byte slots
+        // (at any alignment; not through the LDS variant or element-wise).
         Plan p;
         st = make_plan(ptrs, 2 * nranks, nranks, 1, count, count, dtype, op, tuning, kModeReduce,
                        p);
