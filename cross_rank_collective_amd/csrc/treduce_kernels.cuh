@@ -53,7 +53,12 @@
 // Ragged edges.  Full 16-byte slots form the main tiles.  They are numbered
 // from an aligned origin below the data (1 KiB, 128 bytes or 16 bytes, the
 // coarsest at which every buffer has the same offset), so every wave's run
-// is aligned; the slots before the data are skipped.  Separate tail tiles
+// is aligned; the slots before the data are skipped.  Buffers with no offset
+// in common take dst's origin, and rows whose pitch is off the 16-byte grid
+// number their slots from each row's start: every access is a byte offset
+// from each buffer's own base, so the other buffers' accesses are simply
+// unaligned, which the hardware serves in the unaligned access mode the HSA
+// ABI enables.  Separate tail tiles
 // -- placed before the main tiles in the grid, so their scattered accesses
 // overlap the streaming -- carry, one item per thread: a row's valid bytes
 // after its last full slot (fewer than 16, at most two exact-size accesses
@@ -62,8 +67,10 @@
 // a slot, at most three aligned accesses), and a row's last few full slots
 // when they would fill at most half of a row tile.  Nothing outside the
 // valid rectangle is touched, and the main tiles are branch-free.  The
-// element-wise path (buffers at different offsets) has no main tiles: its
-// tail tiles carry every element of the rectangle, one element per access.
+// element-wise path (forced, rows that never reach their first 16-byte
+// boundary, or misaligned data through the LDS variant or push-with-add)
+// has no main tiles: its tail tiles carry every element of the rectangle,
+// one element per access.
 //
 // Combines on gfx950 (element type kept after every step):
 //   f32  sum v_add_f32, prod v_mul_f32, max/min v_maximum3_f32 / v_minimum3_f32
@@ -395,9 +402,9 @@ __device__ __forceinline__ void store_partial(rsrc_t r, uint32_t off, u32x4 v) {
 }
 
 // Bytes [LO, 16) of a 16-byte slot (LO a multiple of 2, 0 < LO < 16) in
-// naturally aligned pieces -- 2 bytes at LO when LO is 2 mod 4, then 4 bytes
-// to reach an 8-byte boundary, then 8 -- into the same words of a vector as
-// a whole slot would fill; the bytes before LO are zero.
+// pieces aligned from the slot's start -- 2 bytes at LO when LO is 2 mod 4,
+// then 4 bytes to reach an 8-byte boundary, then 8 -- into the same words of
+// a vector as a whole slot would fill; the bytes before LO are zero.
 template <int LO>
 __device__ __forceinline__ u32x4 load_head(rsrc_t r, uint32_t off) {
     static_assert(LO > 0 && LO < 16 && LO % 2 == 0, "head range");

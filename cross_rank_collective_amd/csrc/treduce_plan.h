@@ -27,7 +27,9 @@ struct FastDiv {
 // it): the 16-byte slots of a row (or span) are numbered from that boundary,
 // the ones before the data are skipped, and a row that starts inside a slot
 // begins with a head -- so every wave's 1 KiB run of slots is one aligned
-// KiB, or at least whole cache lines.
+// KiB, or at least whole cache lines.  With no common offset the base is
+// dst's boundary (the sources' accesses unaligned), and with a pitch off the
+// 16-byte grid each row's slots start at the row (every access unaligned).
 struct KArgs {
     // src[0] is the root's buffer, then the other ranks in ascending order:
     // the kernels fold src[0], src[1], ... in index order.
