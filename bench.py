@@ -17,6 +17,10 @@ and push-with-add by atomics (N source reads + one read and one write of dst
 per element, the least any order of the additions must move); memcpy times
 the runtime's device-to-device copy of one buffer, as a context ceiling.
 
+Steps default to 200 timed calls after W warm-up calls, and to 1000 for a
+workload whose step moves less than 64 MiB (the two small ones), whose
+launches last a few microseconds.
+
 When one set of input and output buffers fits in the 256 MB Infinity Cache,
 the steps rotate over enough copies of it (``--sets``, default automatic) to
 touch at least 1 GiB between two uses of a set, so the figure is an HBM one;
@@ -44,6 +48,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 MODES = ["treduce", "allreduce", "reduce_scatter_ring", "accumulate_add", "memcpy"]
 MALL_BYTES = 256 << 20   # MI355X Infinity Cache
 ROTATE_BYTES = 1 << 30   # rotate input sets until the steps touch at least this much
+SMALL_STEP_BYTES = 64 << 20  # steps moving less than this are timed 1000 times by default
 MAX_SETS = 64
 # The kernel each mode launches (one launch per call at the bench's sizes).
 MODE_KERNEL = {"treduce": "treduce_kernel", "allreduce": "treduce_kernel",
@@ -290,7 +295,9 @@ def cpu_baseline(w, op, srcs, gpu_dst_bits, target_s: float = 10.0):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 200, or 1000 for a workload whose step "
+                         "moves less than 64 MiB, whose launches are short and noisy)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--op", default=None)
@@ -334,6 +341,8 @@ def main() -> int:
     dt, opc = B.DTYPES[w.dtype], B.OPS[op]
     mode = args.mode
     algo_bytes = algorithmic_bytes(w, mode)
+    if args.steps is None:
+        args.steps = 1000 if algo_bytes < SMALL_STEP_BYTES else 200
     # Input sets: when one set of buffers fits in the Infinity Cache, the
     # steps rotate over copies so that every step reads from HBM.
     set_bytes = (2 if mode == "memcpy" else w.nranks + 1) * w.buffer_elems * w.esize
