@@ -7,10 +7,11 @@
 // slice the contributions land in an unspecified order; on one GPU the N
 // pushes are the N source buffers and the slice is dst.
 //
-// Each workgroup pushes one rank's tile (blockIdx.y = rank): a 16-byte slot
-// is loaded from that rank's buffer and added into dst with one device-scope
-// atomic per 32-bit word (global_atomic_add_f32, global_atomic_pk_add_f16,
-// global_atomic_pk_add_bf16, global_atomic_add_u32).  A 16-bit element that
+// Each workgroup pushes one rank's tile of 64 16-byte slots (blockIdx.y =
+// rank): the tile's 32-bit words are loaded from that rank's buffer and added
+// into dst with one device-scope atomic per word (global_atomic_add_f32,
+// global_atomic_pk_add_f16, global_atomic_pk_add_bf16, global_atomic_add_u32),
+// consecutive lanes on consecutive words.  A 16-bit element that
 // does not fill its 32-bit word (row remainders, the element-wise path) is
 // added with a compare-and-swap loop on the containing word that rewrites
 // only its own half, so the neighbouring half keeps its bits exactly.  The
@@ -82,12 +83,21 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const KArgs a) {
         if constexpr (VEC) {
             const uint32_t tails = a.total_tiles - a.main_tiles;  // issued first, as in treduce_kernel
             if (t >= tails) {
-                const uint32_t off =
-                    slot_offset<WALK>(a, (t - tails) * (uint32_t)kBlock + threadIdx.x);
-                if (off != kOutOfRange) {
-                    const u32x4 x = load16(rs, off);
+                // The tile's 64 slots as 256 32-bit words, word j of the tile
+                // taken by lane j % 64 in step j / 64: every load and atomic
+                // instruction of the wave covers 256 contiguous bytes (16
+                // slots), two cache lines, where 16 bytes per lane would
+                // spread each instruction's atomics over eight lines -- on
+                // MI355X four times slower at the L2's atomic units.
+                const uint32_t slot0 = (t - tails) * (uint32_t)kBlock;
+                const uint32_t lane = threadIdx.x, byte_in_slot = 4u * (lane & 3u);
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) atomic_add_word<DT>(d + off + 4 * w, x[w]);
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t off =
+                        slot_offset<WALK>(a, slot0 + (uint32_t)(w * 16) + (lane >> 2));
+                    if (off != kOutOfRange)
+                        atomic_add_word<DT>(d + off + byte_in_slot,
+                                            load_elem<4>(rs, off + byte_in_slot));
                 }
             } else {
                 const uint32_t q = t * (uint32_t)kBlock + threadIdx.x;

@@ -149,8 +149,10 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
     // not a multiple of 16 bytes number their slots from each row's start.
     // Measured on MI355X against one element per slot: +14-23% for 2-byte
     // types and odd pitches, level for 4-byte types at N = 16.  Push-with-add
-    // (whose atomics need naturally aligned words) and the LDS variant (whose
-    // loads go straight to LDS) keep the shared-offset rule.
+    // takes dst's alignment too (only its source loads go unaligned; its
+    // atomics stay on aligned words) but not odd pitches, which would move
+    // its atomics off their words; the LDS variant (whose loads go straight
+    // to LDS) keeps the shared-offset rule.
     bool use_vec = (flags & PTORED_FORCE_ELEMENTWISE) == 0;
     auto common_offset = [&](uintptr_t align) {
         const uintptr_t off = reinterpret_cast<uintptr_t>(ptrs[0]) & (align - 1u);
@@ -165,7 +167,8 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         return (int)(reinterpret_cast<uintptr_t>(ptrs[nptrs - 1]) & (align - 1u));
     };
     const bool lds = (flags & PTORED_LDS_PINGPONG) != 0 && mode == kModeReduce && nranks > 1;
-    const bool unaligned_ok = mode != kModeAccumulate && !lds;
+    const bool odd_pitch = p.rows_mode && ((ld * p.esize) & 15) != 0;
+    const bool unaligned_ok = !lds && !(mode == kModeAccumulate && odd_pitch);
     int lead = use_vec ? common_offset(16) : -1;
     if (lead >= 0) {
         const int kib = common_offset(1024), line = common_offset(128);
@@ -175,7 +178,7 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
             lead = line;
         }
     } else if (use_vec && unaligned_ok) {
-        if (p.rows_mode && ((ld * p.esize) & 15) != 0) {
+        if (odd_pitch) {
             lead = 0;  // slots from each row's start
         } else {
             const int kib = anchor_offset(1024), line = anchor_offset(128);

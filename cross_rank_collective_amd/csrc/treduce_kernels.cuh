@@ -68,7 +68,8 @@
 // when they would fill at most half of a row tile.  Nothing outside the
 // valid rectangle is touched, and the main tiles are branch-free.  The
 // element-wise path (forced, rows that never reach their first 16-byte
-// boundary, or misaligned data through the LDS variant or push-with-add)
+// boundary, misaligned data through the LDS variant, or push-with-add with
+// a pitch off the 16-byte grid)
 // has no main tiles: its tail tiles carry every element of the rectangle,
 // one element per access.
 //

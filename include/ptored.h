@@ -119,7 +119,7 @@ typedef enum ptored_status {
  * slots from the row's start, every access unaligned.  A valid row (or
  * span) that does not reach the 16-byte boundary it starts before, the
  * PTORED_LDS_PINGPONG variant on misaligned data and PTORED_FORCE_ELEMENTWISE
- * take an element-wise kernel.
+ * take an element-wise kernel (and push-with-add with an odd pitch).
  */
 int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int64_t rows,
                    int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
@@ -170,8 +170,8 @@ int ptored_treduce_ex(const void* const* srcs, int nranks, int root, void* dst, 
 #define PTORED_PATH_VEC_FIXED 2   /* 16-B vectors, N unrolled at compile time */
 #define PTORED_PATH_VEC_RUNTIME 3 /* 16-B vectors, rank-count loop */
 #define PTORED_PATH_ELEMENTWISE 4 /* one element per slot (forced, rows shorter than their
-                                     first 16-byte block, or misaligned data through the LDS
-                                     variant or push-with-add) */
+                                     first 16-byte block, misaligned data through the LDS
+                                     variant, or push-with-add with an odd pitch) */
 
 typedef struct ptored_plan_info {
     int32_t path;          /* PTORED_PATH_* */
@@ -259,10 +259,11 @@ int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, void* const*
  * exact).  A 16-bit element that does not fill its aligned 32-bit word is
  * added by a compare-and-swap on that word which rewrites only its own half.
  * dst must be device memory of this GPU and must not overlap any source
- * (not even exactly).  The 16-byte kernel needs every buffer at one offset
- * within a 16-byte block and a pitch on the 16-byte grid (its atomics take
- * naturally aligned words); otherwise sources are added element by
- * element.  Other arguments and errors as ptored_treduce_ex.
+ * (not even exactly).  The 16-byte kernel keeps dst aligned (sources at
+ * other offsets are read unaligned) and needs a pitch on the 16-byte grid,
+ * so that its atomics stay on naturally aligned words; with an odd pitch
+ * the sources are added element by element.  Other arguments and errors as
+ * ptored_treduce_ex.
  */
 int ptored_accumulate_add(const void* const* srcs, int nranks, void* dst, int64_t rows,
                           int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
