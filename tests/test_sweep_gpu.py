@@ -4,7 +4,8 @@ in-place aliasing, forcing flags, grid policies and launch windows drawn
 together, each call checked against the oracle.
 
 Bar as in the parity tests: bit-exact (NaN by NaN-ness) for the reduction,
-the allreduce and the reduce-scatter, exact for i32 push-with-add; cells
+the allreduce and the reduce-scatter, exact for i32 push-with-add and within
+the rounding of N additions in any order for float push-with-add; cells
 outside the valid rectangle, guard bands and sources untouched.
 """
 
@@ -235,3 +236,42 @@ def test_sweep_accumulate_i32():
                               valid_rows=vr, valid_cols=vc)
         assert np.array_equal(dd.download("i32"), want), label
         assert dd.guards_intact(), label
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_sweep_accumulate_float(dtype):
+    """Float push-with-add: the additions land in any order, so each valid
+    element must lie within the rounding of N additions of the exact sum;
+    everything outside the valid rectangle keeps its bits."""
+    from tests.gpu_helpers import bits
+    from tests.test_collectives_gpu import TINY, UNIT, _finite_values
+    rng = np.random.default_rng({"f32": 9501, "bf16": 9502, "f16": 9503}[dtype])
+    es = ESIZE[dtype]
+    for case in range(40 * SCALE):
+        n = int(rng.choice(RANKS))
+        rows, cols, ld, vr, vc = _shape(rng, es)
+        offs = _offsets(rng, es, n)
+        size = (rows - 1) * ld + cols
+        t = _tuning(rng, size * es)
+        t.blocks_per_cu = 0
+        srcs = [_finite_values(dtype, rng, size) for _ in range(n)]
+        d0 = _finite_values(dtype, rng, size)
+        sb = _upload(srcs, offs[:n])
+        dd = _upload([d0], [offs[n]])[0]
+        label = (f"sweep accumulate#{case} {dtype} N={n} {rows}x{cols} ld={ld} valid={vr}x{vc} "
+                 f"offs={offs[:3]} dst_off={offs[n]} {_tstr(t)}")
+        say(label)
+        st = B.ptored_accumulate_add([b.ptr for b in sb], n, dd.ptr, rows, cols, ld, vr, vc,
+                                     B.DTYPES[dtype], t, _stream())
+        torch.cuda.synchronize()
+        assert st == 0, (label, B.ptored_status_string(st))
+        got = dd.download(dtype)
+        want = d0.copy()
+        exact, absum = oracle.accumulate_add(srcs, want, dtype=dtype, rows=rows, cols=cols,
+                                             ld=ld, valid_rows=vr, valid_cols=vc)
+        m = valid_mask(rows, ld, vr, vc, size)
+        assert np.array_equal(got[~m].view(np.uint8), d0[~m].view(np.uint8)), label
+        assert dd.guards_intact(), label
+        g = oracle.to_double(dtype, bits(dtype, got[m]).astype(np.uint32))
+        bound = n * UNIT[dtype] * absum * 1.0001 + n * TINY[dtype]
+        assert np.all(np.abs(g - exact) <= bound), label
