@@ -351,7 +351,10 @@ def main() -> int:
         nsets = 1 if set_bytes >= MALL_BYTES else min(MAX_SETS, -(-ROTATE_BYTES // set_bytes))
     sets = [(src_t, dst_t)] + [([t.clone() for t in src_t], dst_t.clone())
                                for _ in range(nsets - 1)]
-    set_ptrs = [[t.data_ptr() for t in srcs_k] for srcs_k, _ in sets]
+    # host pointer arrays built once, so the timed calls marshal only scalars
+    set_ptrs = [B.pointer_array([t.data_ptr() for t in srcs_k]) for srcs_k, _ in sets]
+    dst_ptrs = [dst_k.data_ptr() for _, dst_k in sets]
+    cuda_stream = stream.cuda_stream
     residency = "hbm" if nsets * set_bytes >= ROTATE_BYTES else "cache-resident"
     launches = 1
     launch = None
@@ -374,20 +377,18 @@ def main() -> int:
         srcs_k, dst_k = sets[k]
         ptrs = set_ptrs[k]
         if mode == "treduce":
-            return B.ptored_treduce(ptrs, w.nranks, w.root, dst_k.data_ptr(), w.rows, w.cols,
-                                    w.ld, w.valid_rows, w.valid_cols, dt, opc,
-                                    stream.cuda_stream)
+            return B.ptored_treduce(ptrs, w.nranks, w.root, dst_ptrs[k], w.rows, w.cols,
+                                    w.ld, w.valid_rows, w.valid_cols, dt, opc, cuda_stream)
         if mode == "allreduce":
             return B.ptored_allreduce(ptrs, w.nranks, w.root, w.rows, w.cols, w.ld,
-                                      w.valid_rows, w.valid_cols, dt, opc, None,
-                                      stream.cuda_stream)
+                                      w.valid_rows, w.valid_cols, dt, opc, None, cuda_stream)
         if mode == "reduce_scatter_ring":  # in place: segment s back into rank s's buffer
             return B.ptored_reduce_scatter_ring(ptrs, w.nranks, ptrs, w.buffer_elems, dt, opc,
-                                                None, stream.cuda_stream)
+                                                None, cuda_stream)
         if mode == "accumulate_add":
-            return B.ptored_accumulate_add(ptrs, w.nranks, dst_k.data_ptr(), w.rows, w.cols,
+            return B.ptored_accumulate_add(ptrs, w.nranks, dst_ptrs[k], w.rows, w.cols,
                                            w.ld, w.valid_rows, w.valid_cols, dt, None,
-                                           stream.cuda_stream)
+                                           cuda_stream)
         dst_k.copy_(srcs_k[0])  # memcpy: the runtime's device-to-device copy
         return 0
 

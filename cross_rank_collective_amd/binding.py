@@ -106,8 +106,14 @@ def load() -> ctypes.CDLL:
     return lib
 
 
-def _ptrs(srcs: Sequence[int]):
-    return (ctypes.c_void_p * max(1, len(srcs)))(*[int(p) for p in srcs])
+def pointer_array(ptrs: Sequence[int]) -> ctypes.Array:
+    """A host array of device pointers in the ABI's form; the raw calls take
+    one as is, so a caller that repeats a call can build it once."""
+    return (ctypes.c_void_p * max(1, len(ptrs)))(*[int(p) for p in ptrs])
+
+
+def _ptrs(srcs):
+    return srcs if isinstance(srcs, ctypes.Array) else pointer_array(srcs)
 
 
 def ptored_treduce(srcs: Sequence[int], nranks: int, root: int, dst: int, rows: int, cols: int,

@@ -400,3 +400,15 @@ def test_binding_constants_match_the_header():
              if k.startswith("PTORED_PATH_")}
     assert paths == {0: "none", 1: "copy", 2: "vec_fixed", 3: "vec_runtime", 4: "elementwise"}
     assert B.PATHS == paths
+
+
+def test_prebuilt_pointer_array_is_passed_as_is():
+    """Raw calls take a prebuilt pointer array (built once for repeated calls)
+    and plan it like the list it was built from."""
+    arr = B.pointer_array(A[:4])
+    assert B._ptrs(arr) is arr
+    assert list(arr) == list(A[:4])
+    st1, i1 = crc.ptored_treduce_plan(arr, 4, 0, D, 4, 4, 4, 4, 4, 0, 0)
+    st2, i2 = crc.ptored_treduce_plan(A[:4], 4, 0, D, 4, 4, 4, 4, 4, 0, 0)
+    assert st1 == st2 == 0
+    assert (i1.path, i1.slots, i1.lead) == (i2.path, i2.slots, i2.lead)
