@@ -91,26 +91,52 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const KArgs a) {
                 // slots), two cache lines, where 16 bytes per lane would
                 // spread each instruction's atomics over eight lines -- on
                 // MI355X four times slower at the L2's atomic units.
-                const uint32_t slot0 = (t - tails) * (uint32_t)kBlock;
+                // Row tiles: tile = column chunk c of row r, its slots
+                // numbered from the row's slot origin, so every run stays
+                // inside one row and on the line grid.
+                const uint32_t tile = t - tails;
+                uint32_t slot0 = tile * (uint32_t)kBlock, row_off = 0;
+                if constexpr (WALK == kWalkRowTiles) {
+                    const uint32_t row = fast_div(tile, a.div_tiles);
+                    slot0 = (tile - row * a.tiles_per_row) * (uint32_t)kBlock;
+                    row_off = row * a.ld_bytes;
+                }
                 const uint32_t lane = threadIdx.x, byte_in_slot = 4u * (lane & 3u);
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const uint32_t off =
-                        slot_offset<WALK>(a, slot0 + (uint32_t)(w * 16) + (lane >> 2));
+                    const uint32_t v = slot0 + (uint32_t)(w * 16) + (lane >> 2);
+                    uint32_t off;
+                    if constexpr (WALK == kWalkRowTiles) {
+                        off = v < a.slots_per_row && v >= a.slot_skip ? row_off + v * 16u
+                                                                      : kOutOfRange;
+                    } else {
+                        off = slot_offset<WALK>(a, v);
+                    }
                     if (off != kOutOfRange)
                         atomic_add_word<DT>(d + off + byte_in_slot,
                                             load_elem<4>(rs, off + byte_in_slot));
                 }
             } else {
                 const uint32_t q = t * (uint32_t)kBlock + threadIdx.x;
-                if (q < a.ntail) {  // row remainder
+                // Remainders and heads lie in one 16-byte block of dst that
+                // starts on a 16-byte boundary: whole 32-bit words take one
+                // atomic each, only a lone 16-bit element the half-word one.
+                if (q < a.ntail) {  // row remainder: bytes [0, tail_bytes) of its block
                     const uint32_t off = q * a.ld_bytes + a.tail_col_bytes;
-                    for (uint32_t e = 0; e < a.tail_bytes; e += ES)
+                    uint32_t e = 0;
+                    for (; e + 4u <= a.tail_bytes; e += 4u)
+                        atomic_add_word<DT>(d + off + e, load_elem<4>(rs, off + e));
+                    if (e < a.tail_bytes)
                         atomic_add_elem<DT, ES>(d + off + e, load_elem<ES>(rs, off + e));
                 } else if (q - a.ntail < a.nhead) {  // row head: bytes [head_lo, 16)
                     const uint32_t off = (q - a.ntail) * a.ld_bytes + a.head_off;
-                    for (uint32_t e = a.head_lo; e < 16u; e += ES)
+                    uint32_t e = a.head_lo;
+                    if (e & 2u) {
                         atomic_add_elem<DT, ES>(d + off + e, load_elem<ES>(rs, off + e));
+                        e += 2u;
+                    }
+                    for (; e < 16u; e += 4u)
+                        atomic_add_word<DT>(d + off + e, load_elem<4>(rs, off + e));
                 }
             }
         } else {

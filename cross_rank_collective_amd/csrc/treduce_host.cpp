@@ -87,9 +87,10 @@ struct RowSplit {
     int64_t tiles;  // row tiles per row
     int64_t spill;  // slots per row left to the tail tiles
 };
-RowSplit row_split(int64_t numbered, int64_t per_tile) {
+// Push-with-add (`no_spill`) keeps every slot in its row tiles.
+RowSplit row_split(int64_t numbered, int64_t per_tile, bool no_spill = false) {
     const int64_t whole = numbered / per_tile, rem = numbered % per_tile;
-    if (whole >= 1 && rem > 0 && rem * 2 <= per_tile) return {whole, rem};
+    if (!no_spill && whole >= 1 && rem > 0 && rem * 2 <= per_tile) return {whole, rem};
     return {(numbered + per_tile - 1) / per_tile, 0};
 }
 
@@ -239,11 +240,11 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         // few workgroups resident per CU they measured 3-4% faster than the
         // flattened walk on ragged rows.
         p.rows_mode = kWalkFlat;
-        if (p.family != kFamElem && mode != kModeAccumulate && (flags & PTORED_FLAT_WALK) == 0) {
+        if (p.family != kFamElem && (flags & PTORED_FLAT_WALK) == 0) {
             const int64_t numbered = (p.lead + valid_cols * p.esize) / 16;
             const int64_t full = numbered - (p.lead + 15) / 16;
             const int64_t per_tile = (int64_t)kBlock * p.unroll;
-            const RowSplit rs = row_split(numbered, per_tile);
+            const RowSplit rs = row_split(numbered, per_tile, p.accumulate);
             const int64_t busy = full - rs.spill;  // whole slots the row tiles fold
             const bool fills = busy * 8 >= rs.tiles * per_tile * 7 || rs.tiles >= 8;
             if (full > 0 && (fills || (flags & PTORED_ROW_TILES) != 0))
@@ -410,7 +411,7 @@ int launch_rows(const Plan& p, KArgs a, const char* const* ordered, char* dst, i
         a.tail_col_bytes = (uint32_t)last;
     }
     if (p.rows_mode == kWalkRowTiles) {
-        const RowSplit rs = row_split(a.slots_per_row, (int64_t)kBlock * p.unroll);
+        const RowSplit rs = row_split(a.slots_per_row, (int64_t)kBlock * p.unroll, p.accumulate);
         a.tiles_per_row = (uint32_t)rs.tiles;
         a.div_tiles = fast_div_for(a.tiles_per_row);
         if (rs.spill > 0) {

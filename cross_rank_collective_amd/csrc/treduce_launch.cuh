@@ -142,6 +142,8 @@ static int dispatch_accumulate(const Plan& p, const KArgs& a, hipStream_t s) {
     case kWalkFlat:
         return vec ? launch_accumulate<DT, ES, kWalkFlat, true>(a, s)
                    : launch_accumulate<DT, ES, kWalkFlat, false>(a, s);
+    case kWalkRowTiles:  // the element-wise path never takes row tiles
+        return vec ? launch_accumulate<DT, ES, kWalkRowTiles, true>(a, s) : kLaunchNoKernel;
     default: return kLaunchNoKernel;
     }
 }
