@@ -15,8 +15,8 @@
 // does not fill its 32-bit word (row remainders, the element-wise path) is
 // added with a compare-and-swap loop on the containing word that rewrites
 // only its own half, so the neighbouring half keeps its bits exactly; on the
-// element-wise path two neighbouring lanes whose elements fill one word add
-// them together with one packed atomic.  The
+// element-wise path two neighbouring elements that fill one word are added
+// together with one packed atomic.  The
 // order in which ranks' additions land differs from run to run, so float
 // results agree with any fixed order only to within the rounding of N
 // additions; i32 additions wrap and are exact.
@@ -140,33 +140,57 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const KArgs a) {
                 }
             }
         } else {
+            uint32_t off[kElemUnroll];
 #pragma unroll
-            for (int u = 0; u < kElemUnroll; ++u) {
-                const uint32_t q = t * (uint32_t)(kBlock * kElemUnroll) + (uint32_t)(u * kBlock) +
-                                   threadIdx.x;
-                const uint32_t off = tail_offset<WALK, ES>(a, q);
-                if constexpr (ES == 4) {
-                    if (off != kOutOfRange) atomic_add_word<DT>(d + off, load_elem<4>(rs, off));
-                } else {
-                    // 16-bit elements: a lane whose element opens a 32-bit
-                    // word and whose right neighbour holds the word's other
-                    // half adds both with one packed atomic; every other
-                    // element takes the half-word compare-and-swap.  The
-                    // shuffles run on every lane, before any branch.
-                    const bool valid = off != kOutOfRange;
-                    const uint32_t v = valid ? load_elem<2>(rs, off) : 0u;
-                    const uint32_t lane = threadIdx.x;
-                    const uint32_t next_off = (uint32_t)__shfl_down((int)off, 1, kBlock);
-                    const uint32_t next_v = (uint32_t)__shfl_down((int)v, 1, kBlock);
-                    const uint32_t prev_off = (uint32_t)__shfl_up((int)off, 1, kBlock);
-                    const bool opens = (reinterpret_cast<uintptr_t>(d + off) & 3u) == 0u;
-                    const bool leads = valid && opens && lane + 1u < (uint32_t)kBlock &&
-                                       next_off == off + 2u;
-                    const bool led = valid && !opens && lane > 0u && prev_off + 2u == off;
+            for (int u = 0; u < kElemUnroll; ++u)
+                off[u] = tail_offset<WALK, ES>(
+                    a, t * (uint32_t)(kBlock * kElemUnroll) + (uint32_t)(u * kBlock) + threadIdx.x);
+            if constexpr (ES == 4) {
+#pragma unroll
+                for (int u = 0; u < kElemUnroll; ++u)
+                    if (off[u] != kOutOfRange)
+                        atomic_add_word<DT>(d + off[u], load_elem<4>(rs, off[u]));
+            } else {
+                // 16-bit elements: a lane whose element opens a 32-bit word
+                // and whose right neighbour -- the next lane, or lane 0 of
+                // the next slice of the tile for lane 63 -- holds the word's
+                // other half adds both with one packed atomic; every other
+                // element takes the half-word compare-and-swap.  The
+                // shuffles run on every lane, before any branch.
+                uint32_t v[kElemUnroll];
+#pragma unroll
+                for (int u = 0; u < kElemUnroll; ++u)
+                    v[u] = off[u] != kOutOfRange ? load_elem<2>(rs, off[u]) : 0u;
+                const uint32_t lane = threadIdx.x;
+#pragma unroll
+                for (int u = 0; u < kElemUnroll; ++u) {
+                    const bool valid = off[u] != kOutOfRange;
+                    uint32_t next_off = (uint32_t)__shfl_down((int)off[u], 1, kBlock);
+                    uint32_t next_v = (uint32_t)__shfl_down((int)v[u], 1, kBlock);
+                    uint32_t prev_off = (uint32_t)__shfl_up((int)off[u], 1, kBlock);
+                    if (u + 1 < kElemUnroll) {
+                        const uint32_t o = (uint32_t)__shfl((int)off[u + 1], 0, kBlock);
+                        const uint32_t x = (uint32_t)__shfl((int)v[u + 1], 0, kBlock);
+                        if (lane == (uint32_t)kBlock - 1u) {
+                            next_off = o;
+                            next_v = x;
+                        }
+                    } else if (lane == (uint32_t)kBlock - 1u) {
+                        next_off = kOutOfRange;
+                    }
+                    if (u > 0) {
+                        const uint32_t o = (uint32_t)__shfl((int)off[u - 1], kBlock - 1, kBlock);
+                        if (lane == 0u) prev_off = o;
+                    } else if (lane == 0u) {
+                        prev_off = kOutOfRange;
+                    }
+                    const bool opens = (reinterpret_cast<uintptr_t>(d + off[u]) & 3u) == 0u;
+                    const bool leads = valid && opens && next_off == off[u] + 2u;
+                    const bool led = valid && !opens && prev_off + 2u == off[u];
                     if (leads) {
-                        atomic_add_word<DT>(d + off, (v & 0xFFFFu) | (next_v << 16));
+                        atomic_add_word<DT>(d + off[u], (v[u] & 0xFFFFu) | (next_v << 16));
                     } else if (valid && !led) {
-                        atomic_add_elem<DT, ES>(d + off, v);
+                        atomic_add_elem<DT, ES>(d + off[u], v[u]);
                     }
                 }
             }
