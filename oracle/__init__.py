@@ -102,6 +102,34 @@ def treduce(srcs: Sequence[np.ndarray], dst: np.ndarray, *, root: int, dtype: st
         raise ValueError(f"oracle_treduce rejected its arguments (status {rc})")
 
 
+def treduce_banded(srcs: Sequence[np.ndarray], dst: np.ndarray, *, root: int, dtype: str,
+                   op: str, rows: int, cols: int, ld: int, valid_rows: int, valid_cols: int,
+                   threads: int = 8) -> None:
+    """``treduce`` over large buffers: the valid rows are cut into `threads`
+    contiguous bands and each band is one ``treduce`` call on its own thread
+    (the C code runs without the GIL).  Every element is still computed by
+    the same plain loop; bands only partition independent elements."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    _check_buffers(list(srcs) + [dst], dtype, rows, ld, cols)
+    if valid_rows == 0 or valid_cols == 0 or threads <= 1 or valid_rows < 2 * threads:
+        treduce(srcs, dst, root=root, dtype=dtype, op=op, rows=rows, cols=cols, ld=ld,
+                valid_rows=valid_rows, valid_cols=valid_cols)
+        return
+    cuts = [valid_rows * k // threads for k in range(threads + 1)]
+
+    def band(k):
+        r0, r1 = cuts[k], cuts[k + 1]
+        off = r0 * ld
+        size = (r1 - r0 - 1) * ld + cols
+        treduce([s[off:off + size] for s in srcs], dst[off:off + size], root=root,
+                dtype=dtype, op=op, rows=r1 - r0, cols=cols, ld=ld, valid_rows=r1 - r0,
+                valid_cols=valid_cols)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(band, range(threads)))
+
+
 def allreduce_inplace(bufs: Sequence[np.ndarray], *, root: int, dtype: str, op: str, rows: int,
                       cols: int, ld: int, valid_rows: int, valid_cols: int) -> None:
     """Reduce all buffers and write the result back into every one of them."""

@@ -122,5 +122,27 @@ def oracle_reduce(srcs, dtype, op, root, rows, cols, ld, vr, vc, fill_dst):
     return d
 
 
+def host_threads() -> int:
+    """Host cores this process may use, at most 16 (one GPU's share of a box)."""
+    import os
+
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_reduce_banded(srcs, dtype, op, root, rows, cols, ld, vr, vc):
+    """The oracle over a whole (large) workload into a sentinel-filled buffer,
+    in row bands on the host cores."""
+    size = (rows - 1) * ld + cols if rows > 0 else 0
+    d = sentinel(dtype, max(size, 1))
+    oracle.treduce_banded([np.ascontiguousarray(s[:max(size, 1)]) for s in srcs], d, root=root,
+                          dtype=dtype, op=op, rows=rows, cols=cols, ld=ld, valid_rows=vr,
+                          valid_cols=vc, threads=host_threads())
+    return d
+
+
 def sentinel(dtype: str, n: int) -> np.ndarray:
     return np.full(n * ESIZE[dtype], 0xFF, dtype=np.uint8).view(STORAGE[dtype])
