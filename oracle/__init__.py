@@ -24,6 +24,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "treduce_oracle.c")
 _LIB = os.path.join(_HERE, "libtreduce_oracle.so")
+# A separately built copy of the same source (the sanitizer run builds one
+# with -fsanitize=address,undefined) may be named here; it is loaded as is.
+_LIB_OVERRIDE = os.environ.get("PTORED_ORACLE_LIB")
 
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "i32": 3}
 OPS = {"sum": 0, "max": 1, "min": 2, "prod": 3}
@@ -32,25 +35,28 @@ STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16, "i32": np.int
 _lib = None
 
 
-def build() -> str:
+def build(out: str = _LIB, extra_flags: Sequence[str] = ()) -> str:
     """Compile the oracle with gcc (IEEE arithmetic: no contraction, no fast-math)."""
     cmd = [
         "gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-        "-fno-finite-math-only", "-Wall", "-Wextra", "-shared", "-fPIC",
-        "-o", _LIB + ".tmp", _SRC, "-lm",
+        "-fno-finite-math-only", "-Wall", "-Wextra", "-shared", "-fPIC", *extra_flags,
+        "-o", out + ".tmp", _SRC, "-lm",
     ]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
     i64 = ctypes.c_int64
     vp = ctypes.c_void_p
     lib.oracle_treduce.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, vp,
