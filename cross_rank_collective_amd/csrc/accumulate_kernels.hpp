@@ -1,4 +1,4 @@
-// accumulate_kernels.cuh -- push-with-add: dst += src_r for every rank r.
+// accumulate_kernels.hpp -- push-with-add: dst += src_r for every rank r.
 //
 // Source: "Distributed Operators (N6)", PyPTO docs, pld.tile.remote_store /
 // pld.tensor.put with atomic = AtomicType.kAdd: a push that adds into the
@@ -22,7 +22,7 @@
 // additions; i32 additions wrap and are exact.
 #pragma once
 
-#include "treduce_kernels.cuh"
+#include "treduce_kernels.hpp"
 
 namespace ptored {
 

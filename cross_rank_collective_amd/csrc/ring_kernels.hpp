@@ -1,4 +1,4 @@
-// ring_kernels.cuh -- the ring reduce-scatter in one launch.
+// ring_kernels.hpp -- the ring reduce-scatter in one launch.
 //
 // Source: "Distributed Operators (N6)", PyPTO docs, pld.tensor.allreduce in
 // ring mode: the stream is cut into one segment per rank, and segment s
@@ -14,7 +14,7 @@
 // be 16-byte aligned) are folded one per lane in the segment's last tile.
 #pragma once
 
-#include "treduce_kernels.cuh"
+#include "treduce_kernels.hpp"
 
 namespace ptored {
 

@@ -1,7 +1,7 @@
 // treduce_i32.hip -- launchers for i32 elements: the copy and push-with-add
 // kernel instances, and the per-operator selection of the reduction and ring
 // instances (treduce_op.hip).
-#include "treduce_launch.cuh"
+#include "treduce_launch.hpp"
 
 namespace ptored {
 

@@ -1,4 +1,4 @@
-// treduce_kernels.cuh -- gfx950 kernels of the N-way reduction.
+// treduce_kernels.hpp -- gfx950 kernels of the N-way reduction.
 //
 // Sources (cited by title and section):
 //   [TREDUCE]  "CANN PTO-ISA TREDUCE instruction explained" (lpnh.cn article

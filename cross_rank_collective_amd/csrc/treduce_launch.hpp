@@ -1,4 +1,4 @@
-// treduce_launch.cuh -- kernel selection.
+// treduce_launch.hpp -- kernel selection.
 //
 // Maps a Plan onto one template instance: the rank count N is a
 // compile-time constant for 1 <= N <= 16 (fully unrolled loads); larger or
@@ -9,9 +9,9 @@
 // type (treduce_<type>.hip), so the units compile in parallel.
 #pragma once
 
-#include "accumulate_kernels.cuh"
-#include "ring_kernels.cuh"
-#include "treduce_kernels.cuh"
+#include "accumulate_kernels.hpp"
+#include "ring_kernels.hpp"
+#include "treduce_kernels.hpp"
 
 namespace ptored {
 

@@ -1,7 +1,7 @@
 // treduce_op.hip -- reduction and ring kernel instances of one (element type,
 // operator) pair.  The build compiles this file once per pair, with
 // -DPTORED_INST_DT=<a ptored_dtype name> -DPTORED_INST_OP=<a ptored_op name>.
-#include "treduce_launch.cuh"
+#include "treduce_launch.hpp"
 
 #if !defined(PTORED_INST_DT) || !defined(PTORED_INST_OP)
 #error "treduce_op.hip needs -DPTORED_INST_DT=<ptored_dtype> -DPTORED_INST_OP=<ptored_op>"

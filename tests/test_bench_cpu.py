@@ -50,3 +50,106 @@ def test_comment_and_layout_edits_keep_the_source_hash():
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only("return x + 2;") != bench._code_only("return x + 1;")
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_kernel_instances_are_matched_to_their_entry():
+    w16 = W.find("n16_i32_4096x4096")
+    w5 = W.find("n8_f16_8192x12288_valid8191x12287")
+    cal = W.find("n1_i32_16384x16384_copy")
+    k = "void ptored::treduce_kernel<{}>(ptored::KArgs)"
+    assert bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, false"), w16, "sum", "treduce")
+    assert not bench.kernel_matches(k.format("3, 1, 4, 16, 1, 0, true, false"), w16, "sum",
+                                    "treduce")
+    assert bench.kernel_matches(k.format("3, 1, 4, 16, 1, 0, true, false"), w16, "max", "treduce")
+    assert not bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, true"), w16, "sum",
+                                    "treduce")
+    assert bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, true"), w16, "sum",
+                                "allreduce")
+    assert bench.kernel_matches(k.format("2, 1, 2, 8, 1, 1, true, false"), w5, "max", "treduce")
+    assert bench.kernel_matches(k.format("3, 0, 4, 1, 2, 0, true, false"), cal, "sum", "treduce")
+    assert not bench.kernel_matches(k.format("3, 0, 4, 1, 2, 0, true, false"), w16, "sum",
+                                    "treduce")
+    assert bench.kernel_matches("void ptored::ring_kernel<3, 0, 4, 16>(ptored::RingArgs)", w16,
+                                "sum", "reduce_scatter_ring")
+    assert bench.kernel_matches("void ptored::accumulate_kernel<3, 4, 0, true>(ptored::KArgs)",
+                                w16, "sum", "accumulate_add")
+    assert not bench.kernel_matches("__amd_rocclr_copyBuffer", w16, "sum", "treduce")
+
+
+def test_default_run_starts_with_the_headline_and_covers_every_config():
+    pairs = bench.default_run()
+    assert pairs[0] == (W.HEADLINE, "sum")
+    want = {(w.name, op) for w in W.WORKLOADS.values() for op in w.ops}
+    assert set(pairs) == want and len(pairs) == len(want)
+
+
+def _write_csv(path, header, rows):
+    import csv
+
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(header)
+        wr.writerows(rows)
+
+
+def test_summarize_counters_scales_by_the_copy_in_the_same_run(monkeypatch, tmp_path):
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    k16 = "void ptored::treduce_kernel<3, 0, 4, 16, 1, 0, true, false>(ptored::KArgs)"
+    kcopy = "void ptored::treduce_kernel<3, 0, 4, 1, 2, 0, true, false>(ptored::KArgs)"
+    gib_kib = 1 << 20
+    _write_csv(tmp_path / "f" / "run_counter_collection.csv", hdr,
+               [[k16, "FETCH_SIZE", 8 * 65536.0], [k16, "FETCH_SIZE", 8 * 65536.0],
+                [kcopy, "FETCH_SIZE", gib_kib / 2], ["other", "FETCH_SIZE", 1.0]])
+    _write_csv(tmp_path / "w" / "run_counter_collection.csv", hdr,
+               [[k16, "WRITE_SIZE", 65536.0], [kcopy, "WRITE_SIZE", gib_kib]])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    out = tmp_path / "out.txt"
+    monkeypatch.setattr(bench, "traffic_path", lambda wl, op, mode: str(out))
+
+    class A:
+        summarize_counters = (str(tmp_path / "f"), str(tmp_path / "w"))
+        mode = "treduce"
+        commands = ["cmd"]
+
+    assert bench.summarize_counters(A) == 0
+    vals = dict(ln.split(" = ") for ln in out.read_text().splitlines() if " = " in ln)
+    assert float(vals["fetch_scale"]) == 2.0 and float(vals["write_scale"]) == 1.0
+    # 16 x 64 MiB read (counted half, scaled by 2) + 64 MiB written
+    assert int(vals["hbm_bytes_per_launch"]) == 17 * 64 * 2 ** 20
+    assert vals["traffic_over_algorithmic"] == "1.0000"
+
+
+def test_summarize_trace_pairs_each_entry_with_its_kernel(monkeypatch, tmp_path):
+    import json
+
+    hdr = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
+           "StdDev"]
+    k16 = "void ptored::treduce_kernel<3, 0, 4, 16, 1, 0, true, false>(ptored::KArgs)"
+    k16max = "void ptored::treduce_kernel<3, 1, 4, 16, 1, 0, true, false>(ptored::KArgs)"
+    _write_csv(tmp_path / "t" / "run_kernel_stats.csv", hdr,
+               [[k16, 10, 1700000, 170000, 50, 160000, 180000, 1],
+                [k16max, 10, 1720000, 172000, 50, 160000, 180000, 1]])
+    line = {"metric": "m", "value": 6700.0, "ms_per_step": 0.171, "steps": 4, "warmup": 1,
+            "config": {"workload": "n16_i32_4096x4096", "op": "sum", "mode": "treduce"},
+            "configs": {"n16_i32_4096x4096:max": {
+                "workload": "n16_i32_4096x4096", "op": "max", "ms_per_step": 0.1715,
+                "gbs": 6650.0, "steps": 4, "warmup": 1}},
+            "device": {"name": "gpu", "uuid": "u"}}
+    log = tmp_path / "bench.log"
+    log.write_text("noise\n" + json.dumps(line) + "\n")
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+
+    class A:
+        summarize_trace = str(tmp_path / "t")
+        bench_log = str(log)
+        commands = ["rocprofv3", "--kernel-trace"]
+
+    assert bench.summarize_trace(A) == 0
+    # the max entry's kernel (172 us) is longer than its step (171.5 us): flagged
+    for op, avg, within in (("sum", "170.00", "true"), ("max", "172.00", "false")):
+        text = (tmp_path / f"kernel_trace_n16_i32_4096x4096_{op}.txt").read_text()
+        vals = dict(ln.split(" = ") for ln in text.splitlines() if " = " in ln)
+        assert vals["kernel_average_us"] == avg
+        assert vals["kernel_average_within_ms_per_step"] == within
+        assert "uuid u" in text
