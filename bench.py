@@ -67,7 +67,7 @@ SMALL_STEP_BYTES = 64 << 20  # steps moving less than this are timed 1000 times 
 MAX_SETS = 64
 # The kernel each mode launches (one launch per call at the bench's sizes).
 MODE_KERNEL = {"treduce": "treduce_kernel", "allreduce": "treduce_kernel",
-               "reduce_scatter_ring": "ring_kernel", "accumulate_add": "accumulate_kernel",
+               "reduce_scatter_ring": "ring_kernel", "accumulate_add": "treduce_kernel",
                "memcpy": "copyBuffer"}
 
 
@@ -159,13 +159,19 @@ def kernel_template(name: str):
     return m.group(1), [a.strip() for a in m.group(2).split(",")]
 
 
+# The store-mode argument of treduce_kernel: into dst, into every source
+# (the in-place allreduce), added into dst (push-with-add).
+STORE_MODE = {"treduce": "0", "allreduce": "1", "accumulate_add": "2"}
+
+
 def kernel_matches(name: str, w, op: str, mode: str) -> bool:
     """Whether a kernel instance is the one a call of `mode` on workload `w`
-    with operator `op` launches: the reduction and the allreduce run
-    treduce_kernel<type, op, esize, N, ..., store-to-every-source> (N = 0
-    for the runtime rank loop above 16; N = 1 is the copy), the ring
-    ring_kernel<type, op, esize, N>, push-with-add accumulate_kernel<type,
-    esize, ...>, memcpy the runtime's copy kernel."""
+    with operator `op` launches: the reduction, the allreduce and the default
+    push-with-add run treduce_kernel<type, op, esize, N, ..., store mode>
+    (N = 0 for the runtime rank loop above 16; N = 1 is the copy; push-with-
+    add is a Sum), the ring ring_kernel<type, op, esize, N>, per-rank push-
+    with-add accumulate_kernel<type, esize, ...>, memcpy the runtime's copy
+    kernel."""
     if mode == "memcpy":
         return "copyBuffer" in name
     t = kernel_template(name)
@@ -174,12 +180,13 @@ def kernel_matches(name: str, w, op: str, mode: str) -> bool:
     kern, args = t
     dt, es = str(DT_CODE[w.dtype]), str(w.esize)
     nr = str(w.nranks if w.nranks <= 16 else 0)
-    if mode in ("treduce", "allreduce"):
-        return (kern == "treduce_kernel" and args[:4] == [dt, str(OP_CODE[op]), es, nr]
-                and args[-1] == ("true" if mode == "allreduce" else "false"))
     if mode == "reduce_scatter_ring":
         return kern == "ring_kernel" and args == [dt, str(OP_CODE[op]), es, nr]
-    return kern == "accumulate_kernel" and args[:2] == [dt, es]
+    if mode == "accumulate_add" and kern == "accumulate_kernel":
+        return args[:2] == [dt, es]
+    opc = str(OP_CODE["sum" if mode == "accumulate_add" else op])
+    return (kern == "treduce_kernel" and args[:4] == [dt, opc, es, nr]
+            and args[-1] == STORE_MODE[mode])
 
 
 def default_run():
@@ -496,7 +503,7 @@ def time_steps(torch, stream, step, steps: int, warmup: int):
 
 
 def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg: int, dev,
-              srcs):
+              srcs, flags: int = 0):
     """Time one (workload, op, mode) on the GPU; returns its entry and the
     host copy of set 0's output (the reduction's dst, or the first buffer
     after the in-place modes)."""
@@ -518,11 +525,12 @@ def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg
     dst_ptrs = [dst_k.data_ptr() for _, dst_k in sets]
     cuda_stream = stream.cuda_stream
     residency = "hbm" if nsets * set_bytes >= ROTATE_BYTES else "cache-resident"
+    tuning = B.tuning(flags=flags) if flags else None
     launches, launch = 1, None
     if mode == "treduce":
         st, info = B.ptored_treduce_plan([t.data_ptr() for t in src_t], w.nranks, w.root,
                                          dst_t.data_ptr(), w.rows, w.cols, w.ld, w.valid_rows,
-                                         w.valid_cols, dt, opc)
+                                         w.valid_cols, dt, opc, tuning)
         if st != 0:
             raise RuntimeError(B.ptored_status_string(st))
         launches = int(info.launches)
@@ -538,17 +546,21 @@ def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg
         srcs_k, dst_k = sets[k]
         ptrs = set_ptrs[k]
         if mode == "treduce":
+            if tuning is not None:
+                return B.ptored_treduce_ex(ptrs, w.nranks, w.root, dst_ptrs[k], w.rows, w.cols,
+                                           w.ld, w.valid_rows, w.valid_cols, dt, opc, tuning,
+                                           cuda_stream)
             return B.ptored_treduce(ptrs, w.nranks, w.root, dst_ptrs[k], w.rows, w.cols,
                                     w.ld, w.valid_rows, w.valid_cols, dt, opc, cuda_stream)
         if mode == "allreduce":
             return B.ptored_allreduce(ptrs, w.nranks, w.root, w.rows, w.cols, w.ld,
-                                      w.valid_rows, w.valid_cols, dt, opc, None, cuda_stream)
+                                      w.valid_rows, w.valid_cols, dt, opc, tuning, cuda_stream)
         if mode == "reduce_scatter_ring":  # in place: segment s back into rank s's buffer
             return B.ptored_reduce_scatter_ring(ptrs, w.nranks, ptrs, w.buffer_elems, dt, opc,
-                                                None, cuda_stream)
+                                                tuning, cuda_stream)
         if mode == "accumulate_add":
             return B.ptored_accumulate_add(ptrs, w.nranks, dst_ptrs[k], w.rows, w.cols,
-                                           w.ld, w.valid_rows, w.valid_cols, dt, None,
+                                           w.ld, w.valid_rows, w.valid_cols, dt, tuning,
                                            cuda_stream)
         dst_k.copy_(srcs_k[0])  # memcpy: the runtime's device-to-device copy
         return 0
@@ -578,7 +590,9 @@ def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg
         "frac": round(gbs / HBM_PEAK_GBS, 4),
         "elements_per_s": round(w.valid_rows * w.valid_cols / (ms_step * 1e-3), 1),
         "launch": launch,
-        "traffic": stored_traffic(w.name, op, mode) if mode != "memcpy" else None,
+        "tuning_flags": flags,
+        "traffic": (stored_traffic(w.name, op, mode) if mode != "memcpy" and not flags
+                    else None),
     }
     del sets, src_t, dst_t, out
     torch.cuda.empty_cache()
@@ -671,6 +685,9 @@ def main() -> int:
                     help="skip the CPU leg (the oracle's timing and the bit-exact checks)")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the named workload (no other configs, no ceilings)")
+    ap.add_argument("--flags", type=lambda x: int(x, 0), default=0,
+                    help="ptored tuning flags of the named workload's calls (PTORED_* bits, "
+                         "e.g. 0x200 = per-rank push-with-add); 0 = automatic")
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets the steps rotate over (0 = enough to defeat the "
                          "Infinity Cache when one set fits in it)")
@@ -717,7 +734,8 @@ def main() -> int:
 
     steps = steps_for(w, mode)
     srcs = W.make_sources(w)
-    head, head_out = run_entry(torch, B, w, op, mode, steps, args.warmup, args.sets, dev, srcs)
+    head, head_out = run_entry(torch, B, w, op, mode, steps, args.warmup, args.sets, dev, srcs,
+                               args.flags)
 
     line = {
         "metric": METRIC[mode],
@@ -738,6 +756,7 @@ def main() -> int:
             "root", "values", "mode", "algorithmic_bytes_per_step", "launches_per_step",
             "input_sets", "residency")},
         "launch": head["launch"],
+        "tuning_flags": args.flags,
         "pct_of_peak": round(100.0 * head["gbs"] / HBM_PEAK_GBS, 2),
         "elements_per_s": head["elements_per_s"],
         "roofline": {

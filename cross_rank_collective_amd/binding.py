@@ -39,6 +39,7 @@ PTORED_LDS_PINGPONG = 0x20
 PTORED_SEGMENT_LAUNCHES = 0x40
 PTORED_FULL_OCCUPANCY = 0x80
 PTORED_FLAT_WALK = 0x100
+PTORED_ACC_PER_RANK = 0x200
 
 PTORED_MAX_RANKS = 64
 PTORED_WORKGROUP_THREADS = 64  # threads per workgroup of the kernels (one wave)

@@ -87,7 +87,7 @@ struct RowSplit {
     int64_t tiles;  // row tiles per row
     int64_t spill;  // slots per row left to the tail tiles
 };
-// Push-with-add (`no_spill`) keeps every slot in its row tiles.
+// Per-rank push-with-add (`no_spill`) keeps every slot in its row tiles.
 RowSplit row_split(int64_t numbered, int64_t per_tile, bool no_spill = false) {
     const int64_t whole = numbered / per_tile, rem = numbered % per_tile;
     if (!no_spill && whole >= 1 && rem > 0 && rem * 2 <= per_tile) return {whole, rem};
@@ -115,6 +115,7 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
     p.xcd_remap = (flags & PTORED_NO_XCD_REMAP) == 0 && p.blocks_per_cu != 0;
     p.store_all = mode == kModeAllreduce;
     p.accumulate = mode == kModeAccumulate;
+    p.push_per_rank = p.accumulate && (flags & PTORED_ACC_PER_RANK) != 0;
     int64_t mlb = (tuning && tuning->max_launch_bytes > 0) ? tuning->max_launch_bytes
                                                            : kDefaultLaunchBytes;
     mlb = std::min<int64_t>(mlb, kDefaultLaunchBytes);
@@ -196,10 +197,10 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
 
     if (use_vec) {
         p.vec_elems = 16 / p.esize;
-        if (mode == kModeAccumulate) {
+        if (p.push_per_rank) {
             p.family = kFamVecRuntime;  // one source per workgroup row; U = 1
             p.unroll = 1;
-        } else if (nranks == 1) {
+        } else if (nranks == 1 && mode != kModeAccumulate) {
             p.family = kFamCopy;
             p.unroll = unroll_for(1);
         } else if ((flags & PTORED_LDS_PINGPONG) != 0 && mode == kModeReduce) {
@@ -219,8 +220,9 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
         p.unroll = kElemUnroll;
     }
     // Resident workgroups per CU for one-tile-per-block launches of the
-    // 16-byte kernels (not push-with-add, which is bound by its atomics).
-    if (p.family != kFamElem && mode != kModeAccumulate && p.blocks_per_cu == 0 &&
+    // 16-byte kernels (not per-rank push-with-add, which is bound by its
+    // atomics; the folding one moves the reduction's streams).
+    if (p.family != kFamElem && !p.push_per_rank && p.blocks_per_cu == 0 &&
         (flags & PTORED_FULL_OCCUPANCY) == 0) {
         const uint64_t slot_bytes = (uint64_t)kBlock * 16u * (uint64_t)p.unroll;
         const uint64_t streams = p.family == kFamCopy ? 2u
@@ -244,7 +246,7 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
             const int64_t numbered = (p.lead + valid_cols * p.esize) / 16;
             const int64_t full = numbered - (p.lead + 15) / 16;
             const int64_t per_tile = (int64_t)kBlock * p.unroll;
-            const RowSplit rs = row_split(numbered, per_tile, p.accumulate);
+            const RowSplit rs = row_split(numbered, per_tile, p.push_per_rank);
             const int64_t busy = full - rs.spill;  // whole slots the row tiles fold
             const bool fills = busy * 8 >= rs.tiles * per_tile * 7 || rs.tiles >= 8;
             if (full > 0 && (fills || (flags & PTORED_ROW_TILES) != 0))
@@ -411,7 +413,8 @@ int launch_rows(const Plan& p, KArgs a, const char* const* ordered, char* dst, i
         a.tail_col_bytes = (uint32_t)last;
     }
     if (p.rows_mode == kWalkRowTiles) {
-        const RowSplit rs = row_split(a.slots_per_row, (int64_t)kBlock * p.unroll, p.accumulate);
+        const RowSplit rs = row_split(a.slots_per_row, (int64_t)kBlock * p.unroll,
+                                      p.push_per_rank);
         a.tiles_per_row = (uint32_t)rs.tiles;
         a.div_tiles = fast_div_for(a.tiles_per_row);
         if (rs.spill > 0) {

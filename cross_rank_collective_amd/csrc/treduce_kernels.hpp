@@ -485,15 +485,133 @@ __device__ __forceinline__ uint32_t tail_offset(const KArgs& a, uint32_t q) {
     }
 }
 
-// Store one finished slot: to dst, or -- the in-place allreduce of [N6]
-// pld.tensor.allreduce -- back into every source buffer.  Each slot is read
-// from every buffer by the thread that later writes it, so the in-place
-// write never races a read.
-template <bool ALL>
+// ------------------------------------------------------------------------
+// Atomic adds into dst (push-with-add, [N6] pld.tensor.put / remote_store
+// with atomic = kAdd): device-scope, one 32-bit word per atomic --
+// global_atomic_add_f32, global_atomic_pk_add_f16, global_atomic_pk_add_bf16
+// (two 16-bit elements per word) and global_atomic_add_u32.  On gfx950
+// every such atomic is performed past the XCD's L2, at the memory side
+// (measured: WRITE_SIZE counts 4 bytes per atomic), so concurrent pushes
+// from any XCD, stream or kernel into the same words all land.
+// ------------------------------------------------------------------------
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ void atomic_add_word(char* p, uint32_t bits) {
+    if constexpr (DT == PTORED_F32) {
+        __hip_atomic_fetch_add(reinterpret_cast<float*>(p), as_f(bits), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (DT == PTORED_I32) {
+        __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(p), bits, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (DT == PTORED_F16) {
+        __builtin_amdgcn_global_atomic_fadd_v2f16((__attribute__((address_space(1))) h2*)p,
+                                                  as_h2(bits));
+    } else {
+        __builtin_amdgcn_global_atomic_fadd_v2bf16((__attribute__((address_space(1))) s16x2*)p,
+                                                   __builtin_bit_cast(s16x2, bits));
+    }
+}
+
+// a + b for one 16-bit element, rounded to the element type.
+template <int DT>
+__device__ __forceinline__ uint32_t add16(uint32_t a, uint32_t b) {
+    if constexpr (DT == PTORED_F16) {
+        return as_u(as_h2(a) + as_h2(b)) & 0xFFFFu;
+    } else {
+        return bf_pack_rne(bf_lo(a) + bf_lo(b), 0.0f) & 0xFFFFu;
+    }
+}
+
+// Add one element at p (ES bytes; low bits of `bits`) atomically.  A 16-bit
+// element takes a compare-and-swap loop on its aligned 32-bit word that
+// rewrites only its own half, so the neighbouring half keeps its bits.
+template <int DT, int ES>
+__device__ __forceinline__ void atomic_add_elem(char* p, uint32_t bits) {
+    if constexpr (ES == 4) {
+        atomic_add_word<DT>(p, bits);
+    } else {
+        const uintptr_t addr = reinterpret_cast<uintptr_t>(p);
+        uint32_t* w = reinterpret_cast<uint32_t*>(addr & ~uintptr_t(3));
+        const uint32_t shift = (addr & 2u) ? 16u : 0u;
+        uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (;;) {
+            const uint32_t sum = add16<DT>((old >> shift) & 0xFFFFu, bits & 0xFFFFu);
+            const uint32_t desired = (old & ~(0xFFFFu << shift)) | (sum << shift);
+            if (__hip_atomic_compare_exchange_strong(w, &old, desired, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                break;
+        }
+    }
+}
+
+// Element-wise push: lane l adds element v[u] at dst byte offset off[u]
+// (kOutOfRange: none), where off[u] is element base + u * 64 + l of a run
+// of consecutive elements.  For 16-bit types, a lane whose element opens a
+// 32-bit word and whose right neighbour -- the next lane, or lane 0 of the
+// next slice for lane 63 -- holds the word's other half adds both with one
+// packed atomic; every other element takes the half-word compare-and-swap.
+// The shuffles run on every lane, before any branch.
+template <int DT, int ES, int TU>
+__device__ __forceinline__ void push_elements(char* d, const uint32_t (&off)[TU],
+                                              const uint32_t (&v)[TU]) {
+    if constexpr (ES == 4) {
+#pragma unroll
+        for (int u = 0; u < TU; ++u)
+            if (off[u] != kOutOfRange) atomic_add_word<DT>(d + off[u], v[u]);
+    } else {
+        const uint32_t lane = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < TU; ++u) {
+            const bool valid = off[u] != kOutOfRange;
+            uint32_t next_off = (uint32_t)__shfl_down((int)off[u], 1, kBlock);
+            uint32_t next_v = (uint32_t)__shfl_down((int)v[u], 1, kBlock);
+            uint32_t prev_off = (uint32_t)__shfl_up((int)off[u], 1, kBlock);
+            if (u + 1 < TU) {
+                const uint32_t o = (uint32_t)__shfl((int)off[u + 1], 0, kBlock);
+                const uint32_t x = (uint32_t)__shfl((int)v[u + 1], 0, kBlock);
+                if (lane == (uint32_t)kBlock - 1u) {
+                    next_off = o;
+                    next_v = x;
+                }
+            } else if (lane == (uint32_t)kBlock - 1u) {
+                next_off = kOutOfRange;
+            }
+            if (u > 0) {
+                const uint32_t o = (uint32_t)__shfl((int)off[u - 1], kBlock - 1, kBlock);
+                if (lane == 0u) prev_off = o;
+            } else if (lane == 0u) {
+                prev_off = kOutOfRange;
+            }
+            const bool opens = (reinterpret_cast<uintptr_t>(d + off[u]) & 3u) == 0u;
+            const bool leads = valid && opens && next_off == off[u] + 2u;
+            const bool led = valid && !opens && prev_off + 2u == off[u];
+            if (leads) {
+                atomic_add_word<DT>(d + off[u], (v[u] & 0xFFFFu) | (next_v << 16));
+            } else if (valid && !led) {
+                atomic_add_elem<DT, ES>(d + off[u], v[u]);
+            }
+        }
+    }
+}
+
+// Store one finished slot: to dst; back into every source (the in-place
+// allreduce of [N6] pld.tensor.allreduce -- each slot is read from every
+// buffer by the thread that later writes it, so the write never races a
+// read); or added into dst, one atomic per word (push-with-add; dst's slots
+// are 16-byte aligned on this path).
+template <int DT, int SM>
 __device__ __forceinline__ void store_result(const KArgs& a, rsrc_t rd, uint32_t off, u32x4 v) {
-    if constexpr (ALL) {
+    if constexpr (SM == kStoreAll) {
         for (uint32_t k = 0; k < a.nranks; ++k)
             store16<kStoreAllPolicy>(make_rsrc(a.src[k], a.extent), off, v);
+    } else if constexpr (SM == kStoreAdd) {
+        if (off != kOutOfRange) {
+            char* const p = static_cast<char*>(a.dst) + off;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) atomic_add_word<DT>(p + 4 * w, v[w]);
+        }
     } else {
         store16(rd, off, v);
     }
@@ -601,8 +719,48 @@ __device__ __forceinline__ void main_tile_offsets(const KArgs& a, uint32_t t,
     }
 }
 
+// Byte offset of slot s (0 <= s < 64 U) of main tile t, as main_tile_offsets
+// gives it to the lane that folds it.
+template <int U, int WALK>
+__device__ __forceinline__ uint32_t tile_slot_offset(const KArgs& a, uint32_t t, uint32_t s) {
+    if constexpr (WALK == kWalkRowTiles) {
+        const uint32_t row = fast_div(t, a.div_tiles);
+        const uint32_t v = (t - row * a.tiles_per_row) * (uint32_t)(kBlock * U) + s;
+        return v < a.slots_per_row && v >= a.slot_skip ? row * a.ld_bytes + v * 16u
+                                                       : kOutOfRange;
+    } else {
+        return slot_offset<WALK>(a, t * (uint32_t)(kBlock * U) + s);
+    }
+}
+
+// Push-with-add of one main tile's folded slots.  Lane l holds slot
+// 64 u + l; the slots pass through LDS so that word j of each 1 KiB run is
+// added by lane j % 64 in step j / 64: every atomic instruction of the wave
+// covers 256 contiguous bytes (two cache lines).  A lane adding its own
+// slot's four words would spread each instruction over eight lines -- on
+// MI355X four times slower at the memory side, where the atomics are done.
+template <int DT, int U, int WALK>
+__device__ __forceinline__ void push_tile(const KArgs& a, uint32_t t, const u32x4 (&out)[U]) {
+    __shared__ uint32_t xpose[U][256];
+    const uint32_t lane = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; ++u) *reinterpret_cast<u32x4*>(&xpose[u][lane * 4u]) = out[u];
+    __syncthreads();
+    char* const d = static_cast<char*>(a.dst);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t s = (uint32_t)(u * 64 + k * 16) + (lane >> 2);
+            const uint32_t off = tile_slot_offset<U, WALK>(a, t, s);
+            const uint32_t v = xpose[u][k * 64 + lane];
+            if (off != kOutOfRange) atomic_add_word<DT>(d + off + 4u * (lane & 3u), v);
+        }
+    __syncthreads();  // the next tile of a persistent grid rewrites xpose
+}
+
 // One main tile: U full 16-byte slots per thread, NR sources.
-template <int DT, int OP, int NR, int U, int WALK, bool ALL>
+template <int DT, int OP, int NR, int U, int WALK, int SM>
 __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
     uint32_t off[U];
     main_tile_offsets<U, WALK>(a, t, off);
@@ -610,8 +768,12 @@ __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
     u32x4 out[U];
     fold_slots<DT, OP, NR, U>([&](uint32_t k) { return make_rsrc(a.src[k], a.extent); },
                               a.nranks, off, out);
+    if constexpr (SM == kStoreAdd) {
+        push_tile<DT, U, WALK>(a, t, out);
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u) store_result<ALL>(a, rd, off[u], out[u]);
+        for (int u = 0; u < U; ++u) store_result<DT, SM>(a, rd, off[u], out[u]);
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -705,7 +867,7 @@ __device__ __forceinline__ void main_tile_lds(const KArgs& a, uint32_t t, LdsSta
 
 // One tail tile of the element-wise path: kElemUnroll elements per thread,
 // element by element.
-template <int DT, int OP, int ES, int NR, int WALK, bool ALL>
+template <int DT, int OP, int ES, int NR, int WALK, int SM>
 __device__ __forceinline__ void element_tile(const KArgs& a, uint32_t t) {
     constexpr int TU = kElemUnroll;
     const uint32_t base = t * (uint32_t)(kBlock * TU) + threadIdx.x;
@@ -728,9 +890,16 @@ __device__ __forceinline__ void element_tile(const KArgs& a, uint32_t t) {
 #pragma unroll
         for (int u = 0; u < TU; ++u) acc[u].add(x[u]);
     }
+    if constexpr (SM == kStoreAdd) {
+        uint32_t v[TU];
+#pragma unroll
+        for (int u = 0; u < TU; ++u) v[u] = ES == 4 ? acc[u].get() : acc[u].get() & 0xFFFFu;
+        push_elements<DT, ES, TU>(static_cast<char*>(a.dst), off, v);
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < TU; ++u) {
-        if constexpr (ALL) {
+        if constexpr (SM == kStoreAll) {
             for (uint32_t k = 0; k < n; ++k)
                 store_elem<ES, kStoreAllPolicy>(make_rsrc(a.src[k], a.extent), off[u],
                                                 acc[u].get());
@@ -743,7 +912,7 @@ __device__ __forceinline__ void element_tile(const KArgs& a, uint32_t t) {
 // One row remainder of TB bytes (the pages' partial column chunk with a
 // dynamic valid extent): loaded from every source, folded lane-wise in the
 // same order as the main tiles, stored with the same two exact accesses.
-template <int DT, int OP, int NR, int TB, bool ALL>
+template <int DT, int OP, int ES, int NR, int TB, int SM>
 __device__ __forceinline__ void row_tail(const KArgs& a, uint32_t off) {
     const rsrc_t rd = make_rsrc(a.dst, a.extent);
     Acc<DT, OP> acc[4];
@@ -761,9 +930,16 @@ __device__ __forceinline__ void row_tail(const KArgs& a, uint32_t off) {
     u32x4 out;
 #pragma unroll
     for (int w = 0; w < 4; ++w) out[w] = acc[w].get();
-    if constexpr (ALL) {
+    if constexpr (SM == kStoreAll) {
         for (uint32_t k = 0; k < n; ++k)
             store_partial<TB, kStoreAllPolicy>(make_rsrc(a.src[k], a.extent), off, out);
+    } else if constexpr (SM == kStoreAdd) {
+        // whole words, then a lone 16-bit element (the low half of its word)
+        char* const p = static_cast<char*>(a.dst) + off;
+#pragma unroll
+        for (int e = 0; e + 4 <= TB; e += 4) atomic_add_word<DT>(p + e, out[e / 4]);
+        if constexpr (TB % 4 == 2)
+            atomic_add_elem<DT, ES>(p + (TB - 2), out[(TB - 2) / 4] & 0xFFFFu);
     } else {
         store_partial<TB>(rd, off, out);
     }
@@ -773,7 +949,7 @@ __device__ __forceinline__ void row_tail(const KArgs& a, uint32_t off) {
 // source with the pieces of load_head, folded word-wise in the same order
 // as the main tiles (the zero bytes before LO fold among themselves and are
 // never stored), stored with the same pieces.
-template <int DT, int OP, int NR, int LO, bool ALL>
+template <int DT, int OP, int ES, int NR, int LO, int SM>
 __device__ __forceinline__ void row_head(const KArgs& a, uint32_t off) {
     Acc<DT, OP> acc[4];
     {
@@ -790,9 +966,16 @@ __device__ __forceinline__ void row_head(const KArgs& a, uint32_t off) {
     u32x4 out;
 #pragma unroll
     for (int w = 0; w < 4; ++w) out[w] = acc[w].get();
-    if constexpr (ALL) {
+    if constexpr (SM == kStoreAll) {
         for (uint32_t k = 0; k < n; ++k)
             store_head<LO, kStoreAllPolicy>(make_rsrc(a.src[k], a.extent), off, out);
+    } else if constexpr (SM == kStoreAdd) {
+        // a lone 16-bit element at LO (the high half of its word), then whole words
+        char* const p = static_cast<char*>(a.dst) + off;
+        constexpr int A = (LO + 3) / 4 * 4;
+        if constexpr (LO % 4 == 2) atomic_add_elem<DT, ES>(p + LO, out[LO / 4] >> 16);
+#pragma unroll
+        for (int e = A; e < 16; e += 4) atomic_add_word<DT>(p + e, out[e / 4]);
     } else {
         store_head<LO>(make_rsrc(a.dst, a.extent), off, out);
     }
@@ -803,7 +986,7 @@ __device__ __forceinline__ void row_head(const KArgs& a, uint32_t off) {
 // slots (the next nspill): the last few whole slots of every row when they
 // would fill less than half of a row tile of their own, so each lane folds
 // one slot of a different row instead of most lanes of a tile idling.
-template <int DT, int OP, int ES, int NR, bool ALL>
+template <int DT, int OP, int ES, int NR, int SM>
 __device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
     const uint32_t q = t * (uint32_t)kBlock + threadIdx.x;
     if (q >= a.ntail) {
@@ -817,31 +1000,31 @@ __device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
             u32x4 out[1];
             fold_slots<DT, OP, NR, 1>([&](uint32_t r) { return make_rsrc(a.src[r], a.extent); },
                                       a.nranks, off, out);
-            store_result<ALL>(a, make_rsrc(a.dst, a.extent), off[0], out[0]);
+            store_result<DT, SM>(a, make_rsrc(a.dst, a.extent), off[0], out[0]);
             return;
         }
         const uint32_t off = h * a.ld_bytes + a.head_off;
         switch (a.head_lo) {  // uniform over the launch
-        case 2: if constexpr (ES == 2) row_head<DT, OP, NR, 2, ALL>(a, off); break;
-        case 4: row_head<DT, OP, NR, 4, ALL>(a, off); break;
-        case 6: if constexpr (ES == 2) row_head<DT, OP, NR, 6, ALL>(a, off); break;
-        case 8: row_head<DT, OP, NR, 8, ALL>(a, off); break;
-        case 10: if constexpr (ES == 2) row_head<DT, OP, NR, 10, ALL>(a, off); break;
-        case 12: row_head<DT, OP, NR, 12, ALL>(a, off); break;
-        case 14: if constexpr (ES == 2) row_head<DT, OP, NR, 14, ALL>(a, off); break;
+        case 2: if constexpr (ES == 2) row_head<DT, OP, ES, NR, 2, SM>(a, off); break;
+        case 4: row_head<DT, OP, ES, NR, 4, SM>(a, off); break;
+        case 6: if constexpr (ES == 2) row_head<DT, OP, ES, NR, 6, SM>(a, off); break;
+        case 8: row_head<DT, OP, ES, NR, 8, SM>(a, off); break;
+        case 10: if constexpr (ES == 2) row_head<DT, OP, ES, NR, 10, SM>(a, off); break;
+        case 12: row_head<DT, OP, ES, NR, 12, SM>(a, off); break;
+        case 14: if constexpr (ES == 2) row_head<DT, OP, ES, NR, 14, SM>(a, off); break;
         default: break;
         }
         return;
     }
     const uint32_t off = q * a.ld_bytes + a.tail_col_bytes;
     switch (a.tail_bytes) {  // uniform over the launch
-    case 2: if constexpr (ES == 2) row_tail<DT, OP, NR, 2, ALL>(a, off); break;
-    case 4: row_tail<DT, OP, NR, 4, ALL>(a, off); break;
-    case 6: if constexpr (ES == 2) row_tail<DT, OP, NR, 6, ALL>(a, off); break;
-    case 8: row_tail<DT, OP, NR, 8, ALL>(a, off); break;
-    case 10: if constexpr (ES == 2) row_tail<DT, OP, NR, 10, ALL>(a, off); break;
-    case 12: row_tail<DT, OP, NR, 12, ALL>(a, off); break;
-    case 14: if constexpr (ES == 2) row_tail<DT, OP, NR, 14, ALL>(a, off); break;
+    case 2: if constexpr (ES == 2) row_tail<DT, OP, ES, NR, 2, SM>(a, off); break;
+    case 4: row_tail<DT, OP, ES, NR, 4, SM>(a, off); break;
+    case 6: if constexpr (ES == 2) row_tail<DT, OP, ES, NR, 6, SM>(a, off); break;
+    case 8: row_tail<DT, OP, ES, NR, 8, SM>(a, off); break;
+    case 10: if constexpr (ES == 2) row_tail<DT, OP, ES, NR, 10, SM>(a, off); break;
+    case 12: row_tail<DT, OP, ES, NR, 12, SM>(a, off); break;
+    case 14: if constexpr (ES == 2) row_tail<DT, OP, ES, NR, 14, SM>(a, off); break;
     default: break;
     }
 }
@@ -853,9 +1036,10 @@ __device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
 // tiles b, b + G, ... (one tile per block when G equals the tile count).
 // NR == 0: runtime rank count.  VEC: 16-byte main tiles with row-remainder
 // and row-head tail tiles; otherwise element tiles only.
-// WALK: kWalkContig, kWalkRowTiles or kWalkFlat.  ALL: store the result
-// into every source buffer instead of dst (in-place allreduce).
-template <int DT, int OP, int ES, int NR, int U, int WALK, bool VEC, bool ALL>
+// WALK: kWalkContig, kWalkRowTiles or kWalkFlat.  SM: the StoreMode --
+// into dst, into every source buffer (in-place allreduce), or added into
+// dst with atomics (push-with-add, Sum only).
+template <int DT, int OP, int ES, int NR, int U, int WALK, bool VEC, int SM>
 __global__ __launch_bounds__(kBlock) void treduce_kernel(const KArgs a) {
     const uint32_t grid = gridDim.x;
     for (uint32_t t = logical_block(blockIdx.x, grid, a.xcd_remap != 0u); t < a.total_tiles;
@@ -863,12 +1047,12 @@ __global__ __launch_bounds__(kBlock) void treduce_kernel(const KArgs a) {
         if constexpr (VEC) {
             const uint32_t tails = a.total_tiles - a.main_tiles;
             if (t >= tails) {
-                main_tile<DT, OP, NR, U, WALK, ALL>(a, t - tails);
+                main_tile<DT, OP, NR, U, WALK, SM>(a, t - tails);
             } else {
-                row_tail_tile<DT, OP, ES, NR, ALL>(a, t);
+                row_tail_tile<DT, OP, ES, NR, SM>(a, t);
             }
         } else {
-            element_tile<DT, OP, ES, NR, WALK, ALL>(a, t);
+            element_tile<DT, OP, ES, NR, WALK, SM>(a, t);
         }
     }
 }
@@ -886,7 +1070,7 @@ __global__ __launch_bounds__(kBlock) void treduce_lds_kernel(const KArgs a) {
         if (t >= tails) {
             main_tile_lds<DT, OP, S, WALK>(a, t - tails, stages);
         } else {
-            row_tail_tile<DT, OP, ES, 0, false>(a, t);
+            row_tail_tile<DT, OP, ES, 0, kStoreDst>(a, t);
         }
     }
 }

@@ -70,24 +70,29 @@ static int launch(const Plan& p, const KArgs& a, int cu_count, hipStream_t s) {
     return launch_grid<KERNEL>(p, a, a.total_tiles, cu_count, s);
 }
 
-template <int DT, int OP, int ES, int WALK, bool ALL>
+template <int DT, int OP, int ES, int WALK, int SM>
 static int dispatch_n(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
     if (p.family == kFamElem) {
         if constexpr (WALK == kWalkRowTiles) {
             return kLaunchNoKernel;  // the element-wise path never takes row tiles
         } else {
-            return launch<treduce_kernel<DT, OP, ES, 0, 1, WALK, false, ALL>>(p, a, cu, s);
+            return launch<treduce_kernel<DT, OP, ES, 0, 1, WALK, false, SM>>(p, a, cu, s);
         }
+    }
+    if constexpr (SM == kStoreAdd) {  // push-with-add of a single source
+        if (p.family == kFamVecFixed && p.nranks == 1)
+            return launch<treduce_kernel<DT, OP, ES, 1, unroll_for(1), WALK, true, SM>>(p, a, cu,
+                                                                                     s);
     }
     switch (p.family == kFamVecFixed ? p.nranks : 0) {
 #define PTORED_CASE(n) \
-    case n: return launch<treduce_kernel<DT, OP, ES, n, unroll_for(n), WALK, true, ALL>>(p, a, cu, s);
+    case n: return launch<treduce_kernel<DT, OP, ES, n, unroll_for(n), WALK, true, SM>>(p, a, cu, s);
         PTORED_CASE(2) PTORED_CASE(3) PTORED_CASE(4) PTORED_CASE(5) PTORED_CASE(6)
         PTORED_CASE(7) PTORED_CASE(8) PTORED_CASE(9) PTORED_CASE(10) PTORED_CASE(11)
         PTORED_CASE(12) PTORED_CASE(13) PTORED_CASE(14) PTORED_CASE(15) PTORED_CASE(16)
 #undef PTORED_CASE
     case 0:
-        return launch<treduce_kernel<DT, OP, ES, 0, kRuntimeUnroll, WALK, true, ALL>>(p, a, cu, s);
+        return launch<treduce_kernel<DT, OP, ES, 0, kRuntimeUnroll, WALK, true, SM>>(p, a, cu, s);
     default: return kLaunchNoKernel;
     }
 }
@@ -96,9 +101,9 @@ template <int DT, int OP, int ES>
 static int dispatch_op(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
     if (p.store_all) {  // in-place allreduce
         switch (p.rows_mode) {
-        case kWalkContig: return dispatch_n<DT, OP, ES, kWalkContig, true>(p, a, cu, s);
-        case kWalkRowTiles: return dispatch_n<DT, OP, ES, kWalkRowTiles, true>(p, a, cu, s);
-        case kWalkFlat: return dispatch_n<DT, OP, ES, kWalkFlat, true>(p, a, cu, s);
+        case kWalkContig: return dispatch_n<DT, OP, ES, kWalkContig, kStoreAll>(p, a, cu, s);
+        case kWalkRowTiles: return dispatch_n<DT, OP, ES, kWalkRowTiles, kStoreAll>(p, a, cu, s);
+        case kWalkFlat: return dispatch_n<DT, OP, ES, kWalkFlat, kStoreAll>(p, a, cu, s);
         default: return kLaunchNoKernel;
         }
     }
@@ -115,13 +120,26 @@ static int dispatch_op(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
         }
     }
     switch (p.rows_mode) {
-    case kWalkContig: return dispatch_n<DT, OP, ES, kWalkContig, false>(p, a, cu, s);
-    case kWalkRowTiles: return dispatch_n<DT, OP, ES, kWalkRowTiles, false>(p, a, cu, s);
-    default: return dispatch_n<DT, OP, ES, kWalkFlat, false>(p, a, cu, s);
+    case kWalkContig: return dispatch_n<DT, OP, ES, kWalkContig, kStoreDst>(p, a, cu, s);
+    case kWalkRowTiles: return dispatch_n<DT, OP, ES, kWalkRowTiles, kStoreDst>(p, a, cu, s);
+    default: return dispatch_n<DT, OP, ES, kWalkFlat, kStoreDst>(p, a, cu, s);
     }
 }
 
-// Push-with-add: a 2-D grid, one row of workgroups per rank.
+// Push-with-add, default: the reduction kernel folds the call's sources and
+// adds the fold into dst (StoreMode kStoreAdd).
+template <int DT, int ES>
+static int dispatch_push(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
+    switch (p.rows_mode) {
+    case kWalkContig: return dispatch_n<DT, PTORED_SUM, ES, kWalkContig, kStoreAdd>(p, a, cu, s);
+    case kWalkRowTiles:
+        return dispatch_n<DT, PTORED_SUM, ES, kWalkRowTiles, kStoreAdd>(p, a, cu, s);
+    case kWalkFlat: return dispatch_n<DT, PTORED_SUM, ES, kWalkFlat, kStoreAdd>(p, a, cu, s);
+    default: return kLaunchNoKernel;
+    }
+}
+
+// Push-with-add per rank: a 2-D grid, one row of workgroups per rank.
 template <int DT, int ES, int WALK, bool VEC>
 static int launch_accumulate(const KArgs& a, hipStream_t s) {
     void* args[] = {const_cast<KArgs*>(&a)};
@@ -155,14 +173,14 @@ static int dispatch_copy(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
     constexpr int U = unroll_for(1);
     switch (p.rows_mode) {
     case kWalkContig:
-        return launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkContig, true, false>>(p, a,
-                                                                                        cu, s);
+        return launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkContig, true, kStoreDst>>(
+            p, a, cu, s);
     case kWalkRowTiles:
-        return launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkRowTiles, true, false>>(p, a,
-                                                                                          cu, s);
+        return launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkRowTiles, true, kStoreDst>>(
+            p, a, cu, s);
     default:
-        return launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkFlat, true, false>>(p, a, cu,
-                                                                                      s);
+        return launch<treduce_kernel<DT, PTORED_SUM, ES, 1, U, kWalkFlat, true, kStoreDst>>(
+            p, a, cu, s);
     }
 }
 
@@ -203,7 +221,9 @@ static int dispatch_ring(const Plan& p, const RingArgs& a, int cu, hipStream_t s
 
 template <int DT, int ES>
 static int dispatch_dtype(const Plan& p, const KArgs& a, int cu, hipStream_t s) {
-    if (p.accumulate) return dispatch_accumulate<DT, ES>(p, a, s);
+    if (p.accumulate)
+        return p.push_per_rank ? dispatch_accumulate<DT, ES>(p, a, s)
+                               : dispatch_push<DT, ES>(p, a, cu, s);
     if (p.family == kFamCopy) return dispatch_copy<DT, ES>(p, a, cu, s);
     switch (p.op) {
     case PTORED_SUM: return launch_op<DT, PTORED_SUM>(p, a, cu, s);

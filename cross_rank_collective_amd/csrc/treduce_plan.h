@@ -110,6 +110,7 @@ struct Plan {
     bool xcd_remap;
     bool store_all;     // in-place allreduce: the result goes back into every source
     bool accumulate;    // push-with-add: dst += every source, by atomics
+    bool push_per_rank; // push-with-add: one atomic per source element (else fold, then one)
     bool lds_stages;    // main tiles staged through LDS (ping-pong variant)
     int lead;           // vector path: bytes every buffer starts past a 16-byte boundary
     int blocks_per_cu;  // 0: one tile per block; > 0: persistent grid; < 0: at occupancy
@@ -124,6 +125,15 @@ struct Plan {
     int64_t slots;       // whole call
     int64_t max_launch_bytes;
     int64_t launches;
+};
+
+// Where a kernel puts a finished slot: into dst, back into every source
+// (the in-place allreduce), or added into dst with device-scope atomics
+// (push-with-add, after the call's sources are folded).
+enum StoreMode : int {
+    kStoreDst = 0,
+    kStoreAll = 1,
+    kStoreAdd = 2,
 };
 
 // Result of the per-type launch functions.

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PTORED_ABI_VERSION 2
+#define PTORED_ABI_VERSION 3
 /* Largest number of ranks (source buffers) one call accepts. */
 #define PTORED_MAX_RANKS 64
 /* Threads in one workgroup of the library's kernels: one 64-wide wave.
@@ -140,6 +140,10 @@ int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int
                                          one launch over every segment */
 #define PTORED_FLAT_WALK 0x100u       /* 2-D region: slots numbered straight through the rows
                                          instead of row tiles */
+#define PTORED_ACC_PER_RANK 0x200u    /* push-with-add: add every source's elements into dst with
+                                         atomics of their own (N atomics per dst word, as N
+                                         ranks' remote stores land) instead of folding the
+                                         call's sources first and adding the fold (one) */
 #define PTORED_FULL_OCCUPANCY 0x80u   /* let every CU hold as many workgroups as fit, instead of
                                          the 3-16 per CU the automatic launch keeps resident
                                          by reserving LDS it does not use -- a reservation
@@ -253,17 +257,31 @@ int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, void* const*
  * ptored_accumulate_add -- push-with-add into one slice ([N6]
  * pld.tensor.put / remote_store with atomic = kAdd, the pushed data added
  * into the peer's slice): dst[i, j] += src_0[i, j] + ... + src_{N-1}[i, j]
- * over the valid rectangle, every source's contribution applied with
- * device-scope atomic adds, so the additions land in an unspecified order
- * (float results vary within the rounding of N additions; i32 wraps and is
- * exact).  A 16-bit element that does not fill its aligned 32-bit word is
- * added by a compare-and-swap on that word which rewrites only its own half.
- * dst must be device memory of this GPU and must not overlap any source
- * (not even exactly).  The 16-byte kernel keeps dst aligned (sources at
- * other offsets are read unaligned) and needs a pitch on the 16-byte grid,
- * so that its atomics stay on naturally aligned words; with an odd pitch
- * the sources are added element by element.  Other arguments and errors as
- * ptored_treduce_ex.
+ * over the valid rectangle, with device-scope atomic adds, so pushes from
+ * other calls, streams or kernels into the same dst may land at the same
+ * time.
+ *
+ * By default the call's N sources are first folded in rank order exactly as
+ * ptored_treduce folds them with root 0 (element-type rounding after every
+ * step), and the fold f is added into dst with one atomic per 32-bit word:
+ * with no concurrent push, dst[i, j] becomes dst[i, j] + f[i, j] rounded
+ * once to the element type (i32: wrapping).  With PTORED_ACC_PER_RANK in
+ * tuning->flags every source's elements are added with atomics of their
+ * own (N per element, as N ranks' remote stores land), in an order that
+ * varies from run to run: float results then agree with any fixed order
+ * only within the rounding of N additions; i32 stays exact.
+ *
+ * f32 atomics add two binary32 values and round to nearest-even; bf16 and
+ * f16 elements are added two per word by packed atomics.  A 16-bit element
+ * that does not fill its aligned 32-bit word is added by a compare-and-swap
+ * on that word which rewrites only its own half.  dst must be device memory
+ * of this GPU and must not overlap any source (not even exactly).  The
+ * 16-byte kernel keeps dst aligned (sources at other offsets are read
+ * unaligned) and needs a pitch on the 16-byte grid, so that its atomics stay
+ * on naturally aligned words; with an odd pitch the sources are added
+ * element by element.  Other arguments and errors as ptored_treduce_ex.
+ * Bytes moved: N reads of the valid rectangle and one atomic read-modify-
+ * write of dst (N with PTORED_ACC_PER_RANK).
  */
 int ptored_accumulate_add(const void* const* srcs, int nranks, void* dst, int64_t rows,
                           int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,

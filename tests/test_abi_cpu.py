@@ -52,7 +52,7 @@ def test_one_hip_runtime_is_mapped():
 
 
 def test_version_and_limits():
-    assert crc.ptored_abi_version() == 2
+    assert crc.ptored_abi_version() == 3
     assert crc.ptored_max_ranks() == 64
 
 
@@ -395,7 +395,7 @@ def test_binding_constants_match_the_header():
         if hasattr(B, name):
             assert getattr(B, name) == int(value.rstrip("uU"), 0), name
             checked += 1
-    assert checked == 11  # nine flags, the rank limit and the workgroup size
+    assert checked == 12  # ten flags, the rank limit and the workgroup size
     paths = {int(v): k[len("PTORED_PATH_"):].lower() for k, v in defines.items()
              if k.startswith("PTORED_PATH_")}
     assert paths == {0: "none", 1: "copy", 2: "vec_fixed", 3: "vec_runtime", 4: "elementwise"}

@@ -57,17 +57,21 @@ def test_kernel_instances_are_matched_to_their_entry():
     w5 = W.find("n8_f16_8192x12288_valid8191x12287")
     cal = W.find("n1_i32_16384x16384_copy")
     k = "void ptored::treduce_kernel<{}>(ptored::KArgs)"
-    assert bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, false"), w16, "sum", "treduce")
-    assert not bench.kernel_matches(k.format("3, 1, 4, 16, 1, 0, true, false"), w16, "sum",
+    assert bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, 0"), w16, "sum", "treduce")
+    assert not bench.kernel_matches(k.format("3, 1, 4, 16, 1, 0, true, 0"), w16, "sum",
                                     "treduce")
-    assert bench.kernel_matches(k.format("3, 1, 4, 16, 1, 0, true, false"), w16, "max", "treduce")
-    assert not bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, true"), w16, "sum",
+    assert bench.kernel_matches(k.format("3, 1, 4, 16, 1, 0, true, 0"), w16, "max", "treduce")
+    assert not bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, 1"), w16, "sum",
                                     "treduce")
-    assert bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, true"), w16, "sum",
+    assert bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, 1"), w16, "sum",
                                 "allreduce")
-    assert bench.kernel_matches(k.format("2, 1, 2, 8, 1, 1, true, false"), w5, "max", "treduce")
-    assert bench.kernel_matches(k.format("3, 0, 4, 1, 2, 0, true, false"), cal, "sum", "treduce")
-    assert not bench.kernel_matches(k.format("3, 0, 4, 1, 2, 0, true, false"), w16, "sum",
+    assert bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, 2"), w16, "sum",
+                                "accumulate_add")
+    assert not bench.kernel_matches(k.format("3, 0, 4, 16, 1, 0, true, 2"), w16, "sum",
+                                    "treduce")
+    assert bench.kernel_matches(k.format("2, 1, 2, 8, 1, 1, true, 0"), w5, "max", "treduce")
+    assert bench.kernel_matches(k.format("3, 0, 4, 1, 2, 0, true, 0"), cal, "sum", "treduce")
+    assert not bench.kernel_matches(k.format("3, 0, 4, 1, 2, 0, true, 0"), w16, "sum",
                                     "treduce")
     assert bench.kernel_matches("void ptored::ring_kernel<3, 0, 4, 16>(ptored::RingArgs)", w16,
                                 "sum", "reduce_scatter_ring")
@@ -95,8 +99,8 @@ def _write_csv(path, header, rows):
 
 def test_summarize_counters_scales_by_the_copy_in_the_same_run(monkeypatch, tmp_path):
     hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
-    k16 = "void ptored::treduce_kernel<3, 0, 4, 16, 1, 0, true, false>(ptored::KArgs)"
-    kcopy = "void ptored::treduce_kernel<3, 0, 4, 1, 2, 0, true, false>(ptored::KArgs)"
+    k16 = "void ptored::treduce_kernel<3, 0, 4, 16, 1, 0, true, 0>(ptored::KArgs)"
+    kcopy = "void ptored::treduce_kernel<3, 0, 4, 1, 2, 0, true, 0>(ptored::KArgs)"
     gib_kib = 1 << 20
     _write_csv(tmp_path / "f" / "run_counter_collection.csv", hdr,
                [[k16, "FETCH_SIZE", 8 * 65536.0], [k16, "FETCH_SIZE", 8 * 65536.0],
@@ -125,8 +129,8 @@ def test_summarize_trace_pairs_each_entry_with_its_kernel(monkeypatch, tmp_path)
 
     hdr = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
            "StdDev"]
-    k16 = "void ptored::treduce_kernel<3, 0, 4, 16, 1, 0, true, false>(ptored::KArgs)"
-    k16max = "void ptored::treduce_kernel<3, 1, 4, 16, 1, 0, true, false>(ptored::KArgs)"
+    k16 = "void ptored::treduce_kernel<3, 0, 4, 16, 1, 0, true, 0>(ptored::KArgs)"
+    k16max = "void ptored::treduce_kernel<3, 1, 4, 16, 1, 0, true, 0>(ptored::KArgs)"
     _write_csv(tmp_path / "t" / "run_kernel_stats.csv", hdr,
                [[k16, 10, 1700000, 170000, 50, 160000, 180000, 1],
                 [k16max, 10, 1720000, 172000, 50, 160000, 180000, 1]])

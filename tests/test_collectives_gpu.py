@@ -2,9 +2,11 @@
 allreduce, the ring reduce-scatter share, and push-with-add accumulation.
 
 Bar: bit-exact for the allreduce and the reduce-scatter (same fold order and
-arithmetic as the oracle); for push-with-add, bit-exact for i32, and for the
-float types within the rounding bound of N additions in any order (plus N
-times the smallest normal, in case the atomic unit flushes subnormal sums).
+arithmetic as the oracle); for push-with-add here, bit-exact for i32, and for
+the float types within the rounding bound of N additions in any order,
+N * u * sum|x| (u the unit roundoff; an addition whose result is subnormal is
+exact, and the atomics keep subnormals, so no absolute slack is needed).  The
+exact checks of push-with-add are in test_push_gpu.py.
 """
 
 import numpy as np
@@ -151,7 +153,7 @@ def test_collectives_common_lead(dtype):
             assert compare(dtype, got[m], wacc[m]).all(), case
         else:
             g = oracle.to_double(dtype, bits(dtype, got[m]).astype(np.uint32))
-            bound = n * UNIT[dtype] * absum * 1.0001 + n * TINY[dtype]
+            bound = n * UNIT[dtype] * absum * 1.0001
             assert np.all(np.abs(g - exact) <= bound), case
 
 
@@ -333,7 +335,6 @@ def test_reduce_scatter_ring_full_size_i32():
 # ------------------------------------------------------------ push-with-add ---
 
 UNIT = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
-TINY = {"f32": 2.0 ** -126, "f16": 2.0 ** -14, "bf16": 2.0 ** -126}
 
 
 def _finite_values(dtype, rng, n):
@@ -357,7 +358,8 @@ def test_accumulate_add_random(dtype):
         cols = int(rng.integers(1, 700))
         ld = cols + int(rng.choice([0, 1, 8]))
         vr, vc = int(rng.integers(1, rows + 1)), int(rng.integers(1, cols + 1))
-        flags = [0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_FORCE_ROWS][case % 3]
+        flags = [0, B.PTORED_FORCE_ELEMENTWISE, B.PTORED_FORCE_ROWS][case % 3] | (
+            B.PTORED_ACC_PER_RANK if case % 2 else 0)
         size = (rows - 1) * ld + cols
         srcs = [_finite_values(dtype, rng, size) for _ in range(n)]
         d0 = _finite_values(dtype, rng, size)
@@ -381,7 +383,7 @@ def test_accumulate_add_random(dtype):
             assert compare(dtype, got[m], want[m]).all(), case
         else:
             g = oracle.to_double(dtype, bits(dtype, got[m]).astype(np.uint32))
-            bound = n * UNIT[dtype] * absum * 1.0001 + n * TINY[dtype]
+            bound = n * UNIT[dtype] * absum * 1.0001
             assert np.all(np.abs(g - exact) <= bound), case
 
 

@@ -220,6 +220,8 @@ def test_sweep_accumulate_i32():
         size = (rows - 1) * ld + cols
         t = _tuning(rng, size * 4)
         t.blocks_per_cu = 0
+        if case % 2:
+            t.flags |= B.PTORED_ACC_PER_RANK
         srcs = [_rand_elems("i32", rng, size) for _ in range(n)]
         d0 = _rand_elems("i32", rng, size)
         sb = _upload(srcs, offs[:n])
@@ -240,11 +242,13 @@ def test_sweep_accumulate_i32():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_sweep_accumulate_float(dtype):
-    """Float push-with-add: the additions land in any order, so each valid
-    element must lie within the rounding of N additions of the exact sum;
-    everything outside the valid rectangle keeps its bits."""
+    """Float push-with-add.  Folded first (the default): dst + fold(srcs) bit
+    for bit.  Per rank: the additions land in any order, so each valid
+    element must lie within the rounding of N additions of the exact sum.
+    Everything outside the valid rectangle keeps its bits."""
     from tests.gpu_helpers import bits
-    from tests.test_collectives_gpu import TINY, UNIT, _finite_values
+    from tests.test_collectives_gpu import UNIT, _finite_values
+    from tests.test_push_gpu import _fold_then_add
     rng = np.random.default_rng({"f32": 9501, "bf16": 9502, "f16": 9503}[dtype])
     es = ESIZE[dtype]
     for case in range(40 * SCALE):
@@ -254,6 +258,9 @@ def test_sweep_accumulate_float(dtype):
         size = (rows - 1) * ld + cols
         t = _tuning(rng, size * es)
         t.blocks_per_cu = 0
+        per_rank = case % 2 == 1
+        if per_rank:
+            t.flags |= B.PTORED_ACC_PER_RANK
         srcs = [_finite_values(dtype, rng, size) for _ in range(n)]
         d0 = _finite_values(dtype, rng, size)
         sb = _upload(srcs, offs[:n])
@@ -273,5 +280,8 @@ def test_sweep_accumulate_float(dtype):
         assert np.array_equal(got[~m].view(np.uint8), d0[~m].view(np.uint8)), label
         assert dd.guards_intact(), label
         g = oracle.to_double(dtype, bits(dtype, got[m]).astype(np.uint32))
-        bound = n * UNIT[dtype] * absum * 1.0001 + n * TINY[dtype]
+        bound = n * UNIT[dtype] * absum * 1.0001
         assert np.all(np.abs(g - exact) <= bound), label
+        if not per_rank:
+            folded, _ = _fold_then_add(srcs, d0, dtype, rows, cols, ld, vr, vc)
+            assert compare(dtype, got, folded).all(), label
