@@ -248,8 +248,12 @@ def summarize_counters(args) -> int:
     fetch_scale = copy_bytes / (cal_fetch * 1024.0)
     write_scale = copy_bytes / (cal_write * 1024.0)
     mode = args.mode
-    pairs = default_run() if mode == "treduce" else [
-        (w.name, op) for w in W.WORKLOADS.values() for op in w.ops]
+    if mode == "treduce":
+        pairs = default_run()
+    elif mode == "accumulate_add":  # a Sum whatever the workload's operators
+        pairs = [(w.name, "sum") for w in W.WORKLOADS.values()]
+    else:
+        pairs = [(w.name, op) for w in W.WORKLOADS.values() for op in w.ops]
     written = 0
     for wl, op in pairs:
         w = W.find(wl)
