@@ -2,17 +2,19 @@
 from several host threads at once.
 
 Graph capture: the reduction (a launch with the resident-workgroup limit,
-and a ragged 2-D one with row tiles and tail tiles), the in-place allreduce
-and the ring reduce-scatter are captured once with torch.cuda.graph and
-replayed three times, with new inputs written by eager work between the
-replays.  Every replay must equal the same call made eagerly on the same
+and a ragged 2-D one with row tiles and tail tiles), the in-place allreduce,
+the ring reduce-scatter and push-with-add are captured once with
+torch.cuda.graph and replayed three times, with new inputs written by eager
+work between the replays.  Every replay must equal the same call made eagerly on the same
 inputs, bit for bit over the whole output, and sampled rows must equal the
 oracle.  The library records no memset and allocates nothing, so nothing
 it issues is out of place in a graph.
 
 Threads: four host threads, each with its own stream and buffers, call the
 library concurrently (the binding releases the interpreter lock); every
-result must equal the oracle.
+result must equal the oracle.  And four host threads on their own streams
+push-with-add into one shared dst at the same time: with sums that are
+exact in any order, the result must be dst plus every push.
 """
 
 from concurrent.futures import ThreadPoolExecutor
@@ -68,6 +70,8 @@ def test_graph_capture_and_replay():
     ring_src = [_bf16(rng, (rows * cols,)).cuda() for _ in range(4)]
     ring_dst = [torch.full((rows * cols,), -1, dtype=torch.int16,
                            device="cuda").view(torch.bfloat16) for _ in range(4)]
+    acc_src = [_bf16(rng, (rr, rld)).cuda() for _ in range(3)]   # push-with-add, ragged
+    acc_dst = _bf16(rng, (rr, rld)).cuda()
     dt, sum_, mx = B.DTYPES["bf16"], B.OPS["sum"], B.OPS["max"]
 
     def calls(stream):
@@ -79,8 +83,10 @@ def test_graph_capture_and_replay():
                                  dt, sum_, None, stream),
               B.ptored_reduce_scatter_ring([t.data_ptr() for t in ring_src], 4,
                                            [t.data_ptr() for t in ring_dst], rows * cols, dt,
-                                           sum_, None, stream)]
-        assert st == [0, 0, 0, 0], st
+                                           sum_, None, stream),
+              B.ptored_accumulate_add([t.data_ptr() for t in acc_src], 3, acc_dst.data_ptr(),
+                                      rr, rc, rld, rvr, rvc, dt, None, stream)]
+        assert st == [0, 0, 0, 0, 0], st
 
     def fresh_inputs(seed):
         g = np.random.default_rng(seed)
@@ -90,10 +96,12 @@ def test_graph_capture_and_replay():
             t.copy_(_bf16(g, (rr, rld)))
         for t in ring_src:
             t.copy_(_bf16(g, (rows * cols,)))
+        for t in acc_src + [acc_dst]:
+            t.copy_(_bf16(g, (rr, rld)))
 
     def snapshot():
         return [dst.clone(), rdst.clone()] + [b.clone() for b in bufs] + \
-               [d.clone() for d in ring_dst]
+               [d.clone() for d in ring_dst] + [acc_dst.clone()]
 
     calls(torch.cuda.current_stream().cuda_stream)  # warm the per-device caches
     torch.cuda.synchronize()
@@ -104,14 +112,15 @@ def test_graph_capture_and_replay():
     for rep in range(3):
         say(f"graph replay {rep}")
         fresh_inputs(100 + rep)
-        keep = [b.clone() for b in bufs]
+        keep = [b.clone() for b in bufs + [acc_dst]]
         host_srcs = [_host_bits(t) for t in srcs]
         host_rsrcs = [_host_bits(t) for t in rsrcs]
+        host_acc = [_host_bits(t) for t in acc_src + [acc_dst]]
         g.replay()
         torch.cuda.synchronize()
         got = snapshot()
         # the same calls made eagerly on the same inputs
-        for b, k in zip(bufs, keep):
+        for b, k in zip(bufs + [acc_dst], keep):
             b.copy_(k)
         calls(torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
@@ -130,6 +139,17 @@ def test_graph_capture_and_replay():
         for r, w in zip(pick, ref):
             assert compare("bf16", d[r * rld:r * rld + rvc], w).all(), (rep, r)
             assert np.all(d[r * rld + rvc:(r + 1) * rld] == 0xFFFF)  # outside valid: untouched
+        # push-with-add: dst + fold of its sources (rank order), rounded once
+        want = host_acc[3].copy()
+        fold = sentinel("bf16", want.size)
+        oracle.treduce(host_acc[:3], fold, root=0, dtype="bf16", op="sum", rows=rr, cols=rc,
+                       ld=rld, valid_rows=rvr, valid_cols=rvc)
+        m = np.zeros((rr, rld), dtype=bool)
+        m[:rvr, :rvc] = True
+        m = m.reshape(-1)
+        want[m] = oracle.combine_bits("bf16", "sum", want[m].astype(np.uint32),
+                                      fold[m].astype(np.uint32)).astype(np.uint16)
+        assert compare("bf16", _host_bits(got[-1]), want).all(), rep
 
 
 def test_concurrent_host_threads():
@@ -162,3 +182,53 @@ def test_concurrent_host_threads():
     say("four host threads")
     with ThreadPoolExecutor(4) as ex:
         assert all(ex.map(worker, range(4)))
+
+
+@pytest.mark.parametrize("dtype", ["i32", "f16"])
+def test_concurrent_pushes_into_one_dst(dtype):
+    """Four host threads, each on its own stream, push-with-add into the same
+    dst at the same time, several times each (both paths).  The values are
+    small integers, so every order of the additions gives the same exact
+    sum: dst must end as d0 plus every push, none lost."""
+    rng = np.random.default_rng(300 if dtype == "i32" else 301)
+    rows, cols, ld, n, reps = 257, 1000, 1024, 3, 5
+    size = (rows - 1) * ld + cols
+    m = np.zeros((rows, ld), dtype=bool)
+    m[:, :cols] = True
+    m = m.reshape(-1)[:size]
+
+    def draw(k):
+        if dtype == "i32":
+            return rng.integers(-1000, 1000, size).astype(np.int32)
+        return rng.integers(-2, 3, size).astype(np.float16).view(np.uint16)
+
+    d0 = draw(0)
+    dst = torch.from_numpy(d0.view(np.uint8).copy()).cuda()
+    pushes = [[draw(1) for _ in range(n)] for _ in range(4)]
+    dev = [[torch.from_numpy(p.view(np.uint8).copy()).cuda() for p in ps] for ps in pushes]
+    torch.cuda.synchronize()
+
+    def worker(k):
+        stream = torch.cuda.Stream()
+        flags = B.PTORED_ACC_PER_RANK if k % 2 else 0
+        for _ in range(reps):
+            st = B.ptored_accumulate_add([t.data_ptr() for t in dev[k]], n, dst.data_ptr(), rows,
+                                         cols, ld, rows, cols, B.DTYPES[dtype],
+                                         B.tuning(flags=flags), stream.cuda_stream)
+            assert st == 0
+        stream.synchronize()
+        return True
+
+    say(f"four threads pushing into one dst ({dtype})")
+    with ThreadPoolExecutor(4) as ex:
+        assert all(ex.map(worker, range(4)))
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(d0.dtype)
+    if dtype == "i32":
+        total = d0.astype(np.int64) + reps * sum(p.astype(np.int64) for ps in pushes for p in ps)
+        want = np.where(m, total, d0.astype(np.int64)).astype(np.int32)
+    else:
+        vals = d0.view(np.float16).astype(np.float64) + reps * sum(
+            p.view(np.float16).astype(np.float64) for ps in pushes for p in ps)
+        want = np.where(m, vals.astype(np.float16).view(np.uint16), d0)
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))

@@ -1,4 +1,4 @@
-"""Exhaustive pin of the oracle's 16-bit arithmetic (CPU, opt-in).
+"""Exhaustive pin of the oracle's 16-bit arithmetic (CPU; in full opt-in, a slice always).
 
 For every pair of 16-bit patterns (a, b) -- all 2^32 of them -- the oracle's
 Sum and Prod of f16 and of bf16 (the exact result rounded once to the
@@ -13,6 +13,9 @@ against the extremum by an integer order key of the bit patterns (-0 below
 +0; any NaN operand gives a NaN).  NaN results are compared by NaN-ness only.
 
 About a CPU-minute per case on 8 cores: skipped unless PTORED_EXHAUSTIVE=1.
+A slice of it always runs: for each case, every b against four blocks of 256
+values of a -- the non-negative subnormals and zero, their negative twins,
+the block holding +Inf and the NaNs, and one block drawn from a seed.
 """
 
 import os
@@ -24,8 +27,9 @@ import pytest
 
 ROWS_PER_TASK = 256  # values of a per task: 256 x 65536 pairs
 
-pytestmark = pytest.mark.skipif(os.environ.get("PTORED_EXHAUSTIVE") != "1",
-                                reason="exhaustive 2^32-pair check: set PTORED_EXHAUSTIVE=1")
+EXHAUSTIVE = os.environ.get("PTORED_EXHAUSTIVE") == "1"
+CASES = [("f16", "sum"), ("f16", "prod"), ("bf16", "sum"), ("bf16", "prod"), ("f16", "max"),
+         ("f16", "min"), ("bf16", "max"), ("bf16", "min")]
 
 
 def _isnan(dtype, bits):
@@ -75,14 +79,31 @@ def _task(args):
     return int(idx.size), [(int(a[i]), int(bb[i]), int(got[i]), int(want[i])) for i in idx[:5]]
 
 
-@pytest.mark.parametrize("dtype,op", [("f16", "sum"), ("f16", "prod"), ("bf16", "sum"),
-                                      ("bf16", "prod"), ("f16", "max"), ("f16", "min"),
-                                      ("bf16", "max"), ("bf16", "min")])
-def test_all_pairs_match_binary32_then_round(dtype, op):
-    tasks = [(dtype, op, a0) for a0 in range(0, 65536, ROWS_PER_TASK)]
-    workers = max(1, min(8, os.cpu_count() or 1))
+def _run(tasks):
+    workers = max(1, min(8, os.cpu_count() or 1, len(tasks)))
     with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
-        results = list(ex.map(_task, tasks))
+        return list(ex.map(_task, tasks))
+
+
+@pytest.mark.skipif(not EXHAUSTIVE, reason="exhaustive 2^32-pair check: set PTORED_EXHAUSTIVE=1")
+@pytest.mark.parametrize("dtype,op", CASES)
+def test_all_pairs_match_binary32_then_round(dtype, op):
+    results = _run([(dtype, op, a0) for a0 in range(0, 65536, ROWS_PER_TASK)])
     total = sum(n for n, _ in results)
     examples = [e for _, ex_ in results for e in ex_][:5]
     assert total == 0, (total, examples)
+
+
+def test_slices_of_all_pairs_match_binary32_then_round():
+    """The exhaustive check on four 256-value blocks of a per case (every b):
+    zero and the positive subnormals, the negative ones, the block of +Inf
+    and the NaNs (0x7C00 for f16, 0x7F80 for bf16), and one seeded block."""
+    rng = np.random.default_rng(4242)
+    tasks = []
+    for dtype, op in CASES:
+        inf_block = (0x7C00 if dtype == "f16" else 0x7F80) // ROWS_PER_TASK * ROWS_PER_TASK
+        drawn = int(rng.integers(0, 65536 // ROWS_PER_TASK)) * ROWS_PER_TASK
+        tasks += [(dtype, op, a0) for a0 in (0, 0x8000, inf_block, drawn)]
+    results = _run(tasks)
+    bad = [(t, n, ex_) for t, (n, ex_) in zip(tasks, results) if n]
+    assert not bad, bad[:3]
