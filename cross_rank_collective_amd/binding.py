@@ -333,8 +333,12 @@ def reduce_scatter_ring(srcs, dsts, op: str = "sum", tuning: Optional[ptored_tun
 def accumulate_add(srcs, dst, valid: Optional[Tuple[int, int]] = None,
                    tuning: Optional[ptored_tuning] = None, stream=None) -> None:
     """Push-with-add: dst += every source over the valid rectangle, by
-    device-scope atomics (the additions land in an unspecified order).
-    Geometry and stream as ``treduce``; dst may not be a source."""
+    device-scope atomics, so pushes from other calls or streams into the same
+    dst may land meanwhile.  The sources are folded in rank order first and
+    the fold is added with one atomic per word; with
+    ``tuning(flags=PTORED_ACC_PER_RANK)`` every source's elements are added
+    with atomics of their own.  Geometry and stream as ``treduce``; dst may
+    not be a source."""
     import torch
 
     if len(srcs) == 0:
