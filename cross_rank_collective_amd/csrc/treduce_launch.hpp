@@ -26,6 +26,7 @@ namespace ptored {
 template <auto KERNEL, class ARGS>
 static int launch_grid(const Plan& p, const ARGS& a, uint64_t tiles, int cu_count,
                        hipStream_t s) {
+    if (tiles == 0) return kLaunchOk;  // nothing to do: every launched block has a tile
     uint64_t grid = tiles;
     if (p.blocks_per_cu != 0) {
         int per_cu = p.blocks_per_cu;
@@ -43,7 +44,6 @@ static int launch_grid(const Plan& p, const ARGS& a, uint64_t tiles, int cu_coun
         const uint64_t cap = (uint64_t)cu_count * (uint64_t)per_cu;
         if (grid > cap) grid = cap;
     }
-    if (grid < 1) grid = 1;
     uint32_t shmem = 0;
     if (p.cap_lds > 0 && tiles >= p.cap_min_tiles) {
         // the kernel's own static LDS counts toward the reservation; when it
