@@ -667,7 +667,8 @@ def measure_ceilings(torch, B, dev, steps: int, warmup: int):
 
 def device_identity(torch, dev) -> dict:
     p = torch.cuda.get_device_properties(dev)
-    return {"name": p.name, "arch": getattr(p, "gcnArchName", "?"),
+    arch = getattr(p, "gcnArchName", "?")
+    return {"name": p.name or arch.split(":")[0], "arch": arch,
             "uuid": str(getattr(p, "uuid", "?")),
             "pci": f"{getattr(p, 'pci_domain_id', 0):04x}:{getattr(p, 'pci_bus_id', 0):02x}:"
                    f"{getattr(p, 'pci_device_id', 0):02x}",
