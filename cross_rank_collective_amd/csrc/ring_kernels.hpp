@@ -23,7 +23,11 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(const RingArgs a) {
     const uint32_t grid = gridDim.x;
     const uint32_t total = a.nseg * a.tiles_per_seg;
     const uint32_t n = NR > 0 ? (uint32_t)NR : a.nranks;
-    for (uint32_t t = logical_block(blockIdx.x, grid, a.xcd_remap != 0u); t < total; t += grid) {
+    // Every launched block's first tile exists (at most one block per tile,
+    // no launch without tiles), so it is taken without a check, as in
+    // treduce_kernel; `continue` below moves on to the next tile.
+    uint32_t t = logical_block(blockIdx.x, grid, a.xcd_remap != 0u);
+    do {
         const uint32_t q = fast_div(t, a.div_seg);
         const uint32_t local = t - q * a.tiles_per_seg;
         const uint32_t s = a.seg0 + q;
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(const RingArgs a) {
             fold_slots<DT, OP, NR, 1>(src, n, off, out);
             store16(rd, off[0], out[0]);
         }
-    }
+    } while ((t += grid) < total);
 }
 
 }  // namespace ptored
