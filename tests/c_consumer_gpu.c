@@ -22,6 +22,8 @@ int oracle_reduce_scatter_ring(const void* const* srcs, int nranks, void* const*
 int oracle_accumulate_add(const void* const* srcs, int nranks, void* dst, int64_t rows,
                           int64_t cols, int64_t ld, int64_t valid_rows, int64_t valid_cols,
                           int dtype, double* exact, double* absum);
+void oracle_combine_bits(int dtype, int op, const uint32_t* a, const uint32_t* b, uint32_t* out,
+                         int64_t n);
 
 #define MAXN 16
 #define PAD 64 /* bytes before and after every device buffer */
@@ -265,15 +267,19 @@ static int check_ring(int dtype, int op, int n, int64_t count, hipStream_t st) {
     return ok;
 }
 
-/* i32 push-with-add: wrapping integer sums are exact in any order. */
-static int check_accumulate_i32(int n, shape s, hipStream_t st) {
-    const int64_t size = (s.rows - 1) * s.ld + s.cols, bytes = size * 4;
+/* push-with-add.  Default (the call's sources folded first): with no other
+ * push landing meanwhile, dst becomes dst + fold(srcs) rounded once -- the
+ * oracle's fold with root 0, then its one combine step -- byte for byte.
+ * Per rank (i32 only here): wrapping integer sums, exact in any order. */
+static int check_accumulate(int dtype, int n, shape s, int per_rank, hipStream_t st) {
+    const int es = esize(dtype);
+    const int64_t size = (s.rows - 1) * s.ld + s.cols, bytes = size * es;
     unsigned char* h[MAXN];
     const void *hp[MAXN], *dp[MAXN];
     dbuf d[MAXN];
     for (int r = 0; r < n; ++r) {
         h[r] = malloc((size_t)bytes);
-        fill(PTORED_I32, h[r], size);
+        fill(dtype, h[r], size);
         hp[r] = h[r];
         d[r] = dalloc(bytes, 0);
         HIP_OK(hipMemcpy(d[r].p, h[r], (size_t)bytes, hipMemcpyHostToDevice));
@@ -281,26 +287,52 @@ static int check_accumulate_i32(int n, shape s, hipStream_t st) {
     }
     unsigned char* want = malloc((size_t)bytes);
     unsigned char* got = malloc((size_t)bytes);
-    fill(PTORED_I32, want, size);
+    fill(dtype, want, size);
     dbuf dd = dalloc(bytes, 0);
     HIP_OK(hipMemcpy(dd.p, want, (size_t)bytes, hipMemcpyHostToDevice));
-    printf("accumulate_add i32 n %d shape %lldx%lld\n", n, (long long)s.rows,
-           (long long)s.cols);
+    printf("accumulate_add dtype %d %s n %d shape %lldx%lld\n", dtype,
+           per_rank ? "per rank" : "folded", n, (long long)s.rows, (long long)s.cols);
     fflush(stdout);
-    int st_ = ptored_accumulate_add(dp, n, dd.p, s.rows, s.cols, s.ld, s.vr, s.vc, PTORED_I32,
-                                    NULL, st);
+    const ptored_tuning t = {per_rank ? PTORED_ACC_PER_RANK : 0u, 0, 0};
+    int st_ = ptored_accumulate_add(dp, n, dd.p, s.rows, s.cols, s.ld, s.vr, s.vc, dtype, &t, st);
     if (st_ != PTORED_OK) {
         printf("status %s\n", ptored_status_string(st_));
         return 0;
     }
     HIP_OK(hipStreamSynchronize(st));
-    double* ex = malloc(sizeof(double) * (size_t)(s.vr * s.vc));
-    double* ab = malloc(sizeof(double) * (size_t)(s.vr * s.vc));
-    if (oracle_accumulate_add(hp, n, want, s.rows, s.cols, s.ld, s.vr, s.vc, PTORED_I32, ex,
-                              ab) != 0)
-        return 0;
+    if (per_rank) {
+        double* ex = malloc(sizeof(double) * (size_t)(s.vr * s.vc));
+        double* ab = malloc(sizeof(double) * (size_t)(s.vr * s.vc));
+        if (oracle_accumulate_add(hp, n, want, s.rows, s.cols, s.ld, s.vr, s.vc, dtype, ex, ab) !=
+            0)
+            return 0;
+        free(ex);
+        free(ab);
+    } else {
+        unsigned char* fold = calloc(1, (size_t)bytes);
+        if (oracle_treduce(hp, n, 0, fold, s.rows, s.cols, s.ld, s.vr, s.vc, dtype, PTORED_SUM) !=
+            0)
+            return 0;
+        const int64_t cnt = s.vr * s.vc;
+        uint32_t* a = calloc((size_t)cnt, sizeof(uint32_t));
+        uint32_t* b = calloc((size_t)cnt, sizeof(uint32_t));
+        uint32_t* o = calloc((size_t)cnt, sizeof(uint32_t));
+        for (int64_t i = 0, k = 0; i < s.vr; ++i)
+            for (int64_t j = 0; j < s.vc; ++j, ++k) {
+                memcpy(&a[k], want + (i * s.ld + j) * es, (size_t)es);
+                memcpy(&b[k], fold + (i * s.ld + j) * es, (size_t)es);
+            }
+        oracle_combine_bits(dtype, PTORED_SUM, a, b, o, cnt);
+        for (int64_t i = 0, k = 0; i < s.vr; ++i)
+            for (int64_t j = 0; j < s.vc; ++j, ++k)
+                memcpy(want + (i * s.ld + j) * es, &o[k], (size_t)es);
+        free(fold);
+        free(a);
+        free(b);
+        free(o);
+    }
     HIP_OK(hipMemcpy(got, dd.p, (size_t)bytes, hipMemcpyDeviceToHost));
-    int ok = memcmp(got, want, (size_t)bytes) == 0 && guards_ok(dd, bytes, 0);
+    int ok = same(dtype, got, want, bytes, "accumulate_add") && guards_ok(dd, bytes, 0);
     for (int r = 0; r < n; ++r) {
         HIP_OK(hipFree(d[r].base));
         free(h[r]);
@@ -308,8 +340,6 @@ static int check_accumulate_i32(int n, shape s, hipStream_t st) {
     HIP_OK(hipFree(dd.base));
     free(want);
     free(got);
-    free(ex);
-    free(ab);
     ++cases_run;
     return ok;
 }
@@ -344,8 +374,10 @@ int main(void) {
         if (!check_treduce(dt, PTORED_MAX, 5, 0, SHAPES[1], offs, st)) return 1;
         if (!check_allreduce(dt, PTORED_SUM, 8, 3, SHAPES[0], st)) return 1;
         if (!check_ring(dt, PTORED_MIN, 6, 100003, st)) return 1;
+        for (int k = 0; k < 2; ++k)
+            if (!check_accumulate(dt, 7, SHAPES[k], 0, st)) return 1;
     }
-    if (!check_accumulate_i32(7, SHAPES[0], st)) return 1;
+    if (!check_accumulate(PTORED_I32, 7, SHAPES[0], 1, st)) return 1;
     HIP_OK(hipStreamDestroy(st));
     printf("c consumer ok: %d calls\n", cases_run);
     return 0;
