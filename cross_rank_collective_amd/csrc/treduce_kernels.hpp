@@ -48,7 +48,9 @@
 // is used once); stores are device-scope (sc1), which writes through the
 // XCD's L2 to memory -- on MI355X this measured faster for a read-mostly
 // stream than non-temporal or default stores (the in-place allreduce's N
-// store-backs add nt).
+// store-backs add nt).  Push-with-add replaces the store by device-scope
+// atomic adds on naturally aligned 32-bit words (through global addresses,
+// so those offsets are checked against the work, not the extent).
 //
 // Ragged edges.  Full 16-byte slots form the main tiles.  They are numbered
 // from an aligned origin below the data (1 KiB, 128 bytes or 16 bytes, the
