@@ -216,3 +216,30 @@ def test_push_fold_full_size(name):
     assert np.array_equal(got[~m].view(np.uint8), d0[~m].view(np.uint8))
     ok = compare(w.dtype, got[m], want[m])
     assert ok.all(), (int((~ok).sum()), int(np.argmin(ok)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_push_fold_special_values(dtype):
+    """The default push with arbitrary bit patterns in the sources and in dst
+    (NaN, +-Inf, subnormals, signed zeros among them): dst + fold(srcs)
+    bit for bit, NaN by NaN-ness -- the atomic unit's special cases (-0 plus
+    -0, Inf minus Inf, subnormal sums) match IEEE addition rounded once."""
+    from tests.test_parity_gpu import _rand_elems
+
+    rng = np.random.default_rng({"f32": 111, "bf16": 112, "f16": 113}[dtype])
+    for case, (n, rows, cols, ld, flags) in enumerate([
+            (5, 33, 700, 704, 0), (3, 17, 501, 503, 0), (8, 9, 300, 300, B.PTORED_FORCE_ELEMENTWISE),
+            (2, 64, 1024, 1024, 0)]):
+        size = (rows - 1) * ld + cols
+        srcs = [_rand_elems(dtype, rng, size, wild=0.3) for _ in range(n)]
+        d0 = _rand_elems(dtype, rng, size, wild=0.3)
+        # -0 in dst against folds of -0 (every source -0 there): -0 + -0 must stay -0
+        z = rng.random(size) < 0.02
+        neg0 = np.float32(-0.0) if dtype == "f32" else np.uint16(0x8000)
+        for s_ in srcs + [d0]:
+            s_[z] = neg0
+        got = _run_push(srcs, d0, dtype, rows, cols, ld, rows, cols, [0] * n, 0, flags,
+                        f"push special#{case}")
+        want, m = _fold_then_add(srcs, d0, dtype, rows, cols, ld, rows, cols)
+        ok = compare(dtype, got, want)
+        assert ok.all(), (case, int((~ok).sum()), int(np.argmin(ok)))
