@@ -1,7 +1,9 @@
 """Benchmark of the N-way reduction on one MI355X.
 
 One step = one ptored_treduce call over the whole workload (every source
-read once, dst written once), inputs resident in HBM.  Prints ONE JSON line:
+read once, dst written once), inputs resident in HBM and every step's output
+written to HBM (dst rotated over enough buffers that none is still in the
+256 MB Infinity Cache when it is written again).  Prints ONE JSON line:
 effective HBM GB/s = (N+1) * valid bytes / time of the 16-rank i32 Sum
 workload (the largest N-way reduce), with the roofline of its kernel and the
 CPU oracle timed on a bounded sample as a baseline, and beside it:
@@ -63,6 +65,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 MODES = ["treduce", "allreduce", "reduce_scatter_ring", "accumulate_add", "memcpy"]
 MALL_BYTES = 256 << 20   # MI355X Infinity Cache
 ROTATE_BYTES = 1 << 30   # rotate input sets until the steps touch at least this much
+# Rotate the buffers a step writes until this many bytes are written between
+# two uses of one of them: a dst rewritten back to back stays in the Infinity
+# Cache and never reaches HBM, which a real loop (other work between two
+# reductions) does not see.
+WRITE_ROTATE_BYTES = 2 * MALL_BYTES
+MAX_DSTS = 256
 SMALL_STEP_BYTES = 64 << 20  # steps moving less than this are timed 1000 times by default
 MAX_SETS = 64
 # The kernel each mode launches (one launch per call at the bench's sizes).
@@ -513,22 +521,33 @@ def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg
     after the in-place modes)."""
     stream = torch.cuda.current_stream(dev)
     src_t = [torch.from_numpy(s.view(np.uint8)).to(dev) for s in srcs]
-    dst_t = torch.full((w.buffer_elems * w.esize,), 0xFF, dtype=torch.uint8, device=dev)
+    buf_bytes = w.buffer_elems * w.esize
+    dst_t = torch.full((buf_bytes,), 0xFF, dtype=torch.uint8, device=dev)
     dt, opc = B.DTYPES[w.dtype], B.OPS[op]
     algo_bytes = algorithmic_bytes(w, mode)
-    # When one set of buffers fits in the Infinity Cache, the steps rotate
-    # over copies so that every step reads from HBM.
-    set_bytes = (2 if mode == "memcpy" else w.nranks + 1) * w.buffer_elems * w.esize
-    nsets = sets_arg
-    if nsets <= 0:
+    # Every step reads from and writes to HBM: when one set of buffers fits
+    # in the Infinity Cache the steps rotate over copies of it, and the
+    # buffers a step writes -- dst, or the sources themselves for the
+    # in-place modes -- rotate until WRITE_ROTATE_BYTES are written between
+    # two uses of one.  --sets S instead takes exactly S sets and S dsts.
+    set_bytes = (2 if mode == "memcpy" else w.nranks + 1) * buf_bytes
+    in_place = mode in ("allreduce", "reduce_scatter_ring")
+    written = w.nranks * buf_bytes if mode == "allreduce" else buf_bytes
+    nsets, ndst = sets_arg, sets_arg
+    if sets_arg <= 0:
         nsets = 1 if set_bytes >= MALL_BYTES else min(MAX_SETS, -(-ROTATE_BYTES // set_bytes))
-    sets = [(src_t, dst_t)] + [([t.clone() for t in src_t], dst_t.clone())
-                               for _ in range(nsets - 1)]
+        if in_place:
+            nsets = max(nsets, -(-WRITE_ROTATE_BYTES // written))
+        ndst = nsets if in_place else max(nsets, min(MAX_DSTS, -(-WRITE_ROTATE_BYTES // written)))
+    sets = [src_t] + [[t.clone() for t in src_t] for _ in range(nsets - 1)]
+    dsts = [dst_t] + [dst_t.clone() for _ in range(ndst - 1)]
     # host pointer arrays built once, so the timed calls marshal only scalars
-    set_ptrs = [B.pointer_array([t.data_ptr() for t in srcs_k]) for srcs_k, _ in sets]
-    dst_ptrs = [dst_k.data_ptr() for _, dst_k in sets]
+    set_ptrs = [B.pointer_array([t.data_ptr() for t in srcs_k]) for srcs_k in sets]
+    dst_ptrs = [dst_k.data_ptr() for dst_k in dsts]
     cuda_stream = stream.cuda_stream
-    residency = "hbm" if nsets * set_bytes >= ROTATE_BYTES else "cache-resident"
+    reads_hbm = set_bytes >= MALL_BYTES or nsets * set_bytes >= ROTATE_BYTES
+    writes_hbm = (nsets if in_place else ndst) * written >= WRITE_ROTATE_BYTES
+    residency = "hbm" if reads_hbm and writes_hbm else "cache-resident"
     tuning = B.tuning(flags=flags) if flags else None
     launches, launch = 1, None
     if mode == "treduce":
@@ -546,15 +565,15 @@ def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg
                   "workgroups_per_cu": int(info.wgs_per_cu) or "all that fit",
                   "lead_bytes": int(info.lead), "launches": launches}
 
-    def call(k):
-        srcs_k, dst_k = sets[k]
+    def call(step_no):
+        k, kd = step_no % nsets, step_no % ndst
         ptrs = set_ptrs[k]
         if mode == "treduce":
             if tuning is not None:
-                return B.ptored_treduce_ex(ptrs, w.nranks, w.root, dst_ptrs[k], w.rows, w.cols,
+                return B.ptored_treduce_ex(ptrs, w.nranks, w.root, dst_ptrs[kd], w.rows, w.cols,
                                            w.ld, w.valid_rows, w.valid_cols, dt, opc, tuning,
                                            cuda_stream)
-            return B.ptored_treduce(ptrs, w.nranks, w.root, dst_ptrs[k], w.rows, w.cols,
+            return B.ptored_treduce(ptrs, w.nranks, w.root, dst_ptrs[kd], w.rows, w.cols,
                                     w.ld, w.valid_rows, w.valid_cols, dt, opc, cuda_stream)
         if mode == "allreduce":
             return B.ptored_allreduce(ptrs, w.nranks, w.root, w.rows, w.cols, w.ld,
@@ -563,16 +582,16 @@ def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg
             return B.ptored_reduce_scatter_ring(ptrs, w.nranks, ptrs, w.buffer_elems, dt, opc,
                                                 tuning, cuda_stream)
         if mode == "accumulate_add":
-            return B.ptored_accumulate_add(ptrs, w.nranks, dst_ptrs[k], w.rows, w.cols,
+            return B.ptored_accumulate_add(ptrs, w.nranks, dst_ptrs[kd], w.rows, w.cols,
                                            w.ld, w.valid_rows, w.valid_cols, dt, tuning,
                                            cuda_stream)
-        dst_k.copy_(srcs_k[0])  # memcpy: the runtime's device-to-device copy
+        dsts[kd].copy_(sets[k][0])  # memcpy: the runtime's device-to-device copy
         return 0
 
     nstep = [0]
 
     def step():
-        st = call(nstep[0] % nsets)
+        st = call(nstep[0])
         nstep[0] += 1
         if st != 0:
             raise RuntimeError(B.ptored_status_string(st))
@@ -586,7 +605,8 @@ def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg
         "rows": w.rows, "cols": w.cols, "ld": w.ld, "valid_rows": w.valid_rows,
         "valid_cols": w.valid_cols, "root": w.root, "values": w.recipe,
         "algorithmic_bytes_per_step": algo_bytes, "launches_per_step": launches,
-        "input_sets": nsets, "residency": residency, "steps": steps, "warmup": warmup,
+        "input_sets": nsets, "dst_buffers": None if in_place else ndst,
+        "residency": residency, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
         "step_ms": {"median": round(per_step[len(per_step) // 2], 5),
                     "min": round(per_step[0], 5), "max": round(per_step[-1], 5)},
@@ -598,7 +618,7 @@ def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg
         "traffic": (stored_traffic(w.name, op, mode) if mode != "memcpy" and not flags
                     else None),
     }
-    del sets, src_t, dst_t, out
+    del sets, dsts, src_t, dst_t, out
     torch.cuda.empty_cache()
     return entry, host_out
 
@@ -759,7 +779,7 @@ def main() -> int:
         "config": {k: head[k] for k in (
             "workload", "op", "nranks", "rows", "cols", "ld", "valid_rows", "valid_cols",
             "root", "values", "mode", "algorithmic_bytes_per_step", "launches_per_step",
-            "input_sets", "residency")},
+            "input_sets", "dst_buffers", "residency")},
         "launch": head["launch"],
         "tuning_flags": args.flags,
         "pct_of_peak": round(100.0 * head["gbs"] / HBM_PEAK_GBS, 2),

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(const RingArgs a) {
                 Acc<DT, OP> acc;
                 acc.init(load_elem<ES>(src(0u), off));
                 for (uint32_t k = 1; k < n; ++k) acc.add(load_elem<ES>(src(k), off));
-                store_elem<ES>(rd, off, acc.get());
+                store_elem<ES, store_policy_for(NR)>(rd, off, acc.get());
             }
         } else {
             // slots numbered from the 1 KiB boundary at or below the first
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(const RingArgs a) {
             const uint32_t off[1] = {j < nslots && o >= first ? o : kOutOfRange};
             u32x4 out[1];
             fold_slots<DT, OP, NR, 1>(src, n, off, out);
-            store16(rd, off[0], out[0]);
+            store16<store_policy_for(NR)>(rd, off[0], out[0]);
         }
     } while ((t += grid) < total);
 }

@@ -224,13 +224,16 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
     // atomics; the folding one moves the reduction's streams).
     if (p.family != kFamElem && !p.push_per_rank && p.blocks_per_cu == 0 &&
         (flags & PTORED_FULL_OCCUPANCY) == 0) {
-        const uint64_t slot_bytes = (uint64_t)kBlock * 16u * (uint64_t)p.unroll;
-        const uint64_t streams = p.family == kFamCopy ? 2u
-                                 : mode == kModeAllreduce ? 2u * (uint64_t)nranks
-                                                          : (uint64_t)nranks + 1u;
         const bool runtime_loop =
             p.family == kFamVecRuntime && (!p.lds_stages || nranks > 16);
-        p.wgs_per_cu = wgs_per_cu_for(streams * slot_bytes, mode == kModeAllreduce, runtime_loop);
+        if (runtime_loop) {
+            p.wgs_per_cu = mode == kModeAllreduce ? kRuntimeLoopAllreduceWgs : kRuntimeLoopWgs;
+        } else if (mode == kModeAllreduce) {
+            p.wgs_per_cu = wgs_per_cu_allreduce(2u * (uint64_t)nranks * kBlock * 16u *
+                                                (uint64_t)p.unroll);
+        } else {
+            p.wgs_per_cu = wgs_per_cu_reduce(p.family == kFamCopy ? 1 : nranks);
+        }
     }
     const int64_t vec = p.vec_elems;
     if (p.rows_mode) {
@@ -764,12 +767,8 @@ extern "C" int ptored_reduce_scatter_ring(const void* const* srcs, int nranks, v
         st = make_plan(ptrs, 2 * nranks, nranks, 1, count, count, dtype, op, tuning, kModeReduce,
                        p);
         if (st != PTORED_OK) return st;
-        if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages) {
-            if (p.wgs_per_cu > 0)  // the ring kernel moves one slot per thread
-                p.wgs_per_cu = wgs_per_cu_for((uint64_t)(nranks + 1) * kBlock * 16u, false,
-                                              p.family == kFamVecRuntime);
-            return run_ring(p, srcs, dsts, bounds, count, stream);
-        }
+        if ((p.family == kFamVecFixed || p.family == kFamVecRuntime) && !p.lds_stages)
+            return run_ring(p, srcs, dsts, bounds, count, stream);  // the reduction's residency
     }
     const int es = esize_of(dtype);
     for (int s = 0; s < nranks; ++s) {

@@ -45,10 +45,10 @@
 // hardware drops any access past it (loads return zero, stores are
 // discarded): slots past the end of the work are given an offset beyond
 // the extent instead of a branch.  Source loads are non-temporal (the data
-// is used once); stores are device-scope (sc1), which writes through the
-// XCD's L2 to memory -- on MI355X this measured faster for a read-mostly
-// stream than non-temporal or default stores (the in-place allreduce's N
-// store-backs add nt).  Push-with-add replaces the store by device-scope
+// is used once); stores of dst are non-temporal, or device-scope (sc1: written
+// through the XCD's L2) at one and four ranks, whichever measured faster on
+// MI355X for a dst that goes to HBM on every call; the in-place allreduce's
+// N store-backs take sc1 | nt.  Push-with-add replaces the store by device-scope
 // atomic adds on naturally aligned 32-bit words (through global addresses,
 // so those offsets are checked against the work, not the extent).
 //
@@ -321,14 +321,19 @@ struct Acc<PTORED_BF16, PTORED_MIN> {
 
 // Word 3 of a raw buffer resource: 32-bit data format, no swizzle, stride 0.
 constexpr int kRsrcWord3 = 0x00020000;
-// Cache policy bits of the buffer instructions (gfx950): nt for loads,
-// sc1 (device scope, write-through of the XCD's L2) for stores; the in-place
-// allreduce, which writes N times what it reads once, stores with sc1 | nt
-// (measured 2-4% faster there, 1-5% slower for the single store of the
-// reduction).
+// Cache policy bits of the buffer instructions (gfx950): nt (2) for loads;
+// for stores of dst, nt or sc1 (16: device scope, write-through of the XCD's
+// L2) by rank count, and sc1 | nt for the in-place allreduce's store-backs.
+// Measured on MI355X with dst written to HBM on every call: nt stores ahead
+// by 1-4% from 5 ranks on (and at 2), sc1 ahead at 1 and 4 ranks; the
+// allreduce's sc1 | nt ahead of nt alone.  (A dst rewritten back to back,
+// which stays in the Infinity Cache, favours sc1 throughout.)
 constexpr int kLoadPolicy = 2;
-constexpr int kStorePolicy = 16;
+constexpr int kStoreNt = 2;
+constexpr int kStoreSc1 = 16;
 constexpr int kStoreAllPolicy = 18;
+// Store policy of dst for NR ranks (NR == 0: a runtime count, above 16).
+constexpr int store_policy_for(int nr) { return (nr == 1 || nr == 4) ? kStoreSc1 : kStoreNt; }
 // An offset no launch extent reaches (extents are capped at 2^31 bytes).
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
@@ -341,7 +346,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t extent) {
 __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
 }
-template <int POL = kStorePolicy>
+template <int POL>
 __device__ __forceinline__ void store16(rsrc_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, POL);
 }
@@ -354,7 +359,7 @@ __device__ __forceinline__ uint32_t load_elem(rsrc_t r, uint32_t off) {
         return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kLoadPolicy);
     }
 }
-template <int ES, int POL = kStorePolicy>
+template <int ES, int POL>
 __device__ __forceinline__ void store_elem(rsrc_t r, uint32_t off, uint32_t v) {
     if constexpr (ES == 4) {
         __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, POL);
@@ -384,7 +389,7 @@ __device__ __forceinline__ u32x4 load_partial(rsrc_t r, uint32_t off) {
     }
     return v;
 }
-template <int TB, int POL = kStorePolicy>
+template <int TB, int POL>
 __device__ __forceinline__ void store_partial(rsrc_t r, uint32_t off, u32x4 v) {
     constexpr int big = TB >= 12 ? 12 : (TB >= 8 ? 8 : (TB >= 4 ? 4 : 0));
     if constexpr (big == 12) {
@@ -427,7 +432,7 @@ __device__ __forceinline__ u32x4 load_head(rsrc_t r, uint32_t off) {
     }
     return v;
 }
-template <int LO, int POL = kStorePolicy>
+template <int LO, int POL>
 __device__ __forceinline__ void store_head(rsrc_t r, uint32_t off, u32x4 v) {
     constexpr int A = (LO + 3) / 4 * 4;
     if constexpr (LO % 4 == 2) {
@@ -603,7 +608,7 @@ __device__ __forceinline__ void push_elements(char* d, const uint32_t (&off)[TU]
 // buffer by the thread that later writes it, so the write never races a
 // read); or added into dst, one atomic per word (push-with-add; dst's slots
 // are 16-byte aligned on this path).
-template <int DT, int SM>
+template <int DT, int SM, int NR>
 __device__ __forceinline__ void store_result(const KArgs& a, rsrc_t rd, uint32_t off, u32x4 v) {
     if constexpr (SM == kStoreAll) {
         for (uint32_t k = 0; k < a.nranks; ++k)
@@ -615,7 +620,7 @@ __device__ __forceinline__ void store_result(const KArgs& a, rsrc_t rd, uint32_t
             for (int w = 0; w < 4; ++w) atomic_add_word<DT>(p + 4 * w, v[w]);
         }
     } else {
-        store16(rd, off, v);
+        store16<store_policy_for(NR)>(rd, off, v);
     }
 }
 
@@ -774,7 +779,7 @@ __device__ __forceinline__ void main_tile(const KArgs& a, uint32_t t) {
         push_tile<DT, U, WALK>(a, t, out);
     } else {
 #pragma unroll
-        for (int u = 0; u < U; ++u) store_result<DT, SM>(a, rd, off[u], out[u]);
+        for (int u = 0; u < U; ++u) store_result<DT, SM, NR>(a, rd, off[u], out[u]);
     }
 }
 
@@ -864,7 +869,7 @@ __device__ __forceinline__ void main_tile_lds(const KArgs& a, uint32_t t, LdsSta
     u32x4 out;
 #pragma unroll
     for (int w = 0; w < 4; ++w) out[w] = acc[w].get();
-    store16(make_rsrc(a.dst, a.extent), off, out);
+    store16<store_policy_for(0)>(make_rsrc(a.dst, a.extent), off, out);
 }
 
 // One tail tile of the element-wise path: kElemUnroll elements per thread,
@@ -906,7 +911,7 @@ __device__ __forceinline__ void element_tile(const KArgs& a, uint32_t t) {
                 store_elem<ES, kStoreAllPolicy>(make_rsrc(a.src[k], a.extent), off[u],
                                                 acc[u].get());
         } else {
-            store_elem<ES>(rd, off[u], acc[u].get());
+            store_elem<ES, store_policy_for(NR)>(rd, off[u], acc[u].get());
         }
     }
 }
@@ -943,7 +948,7 @@ __device__ __forceinline__ void row_tail(const KArgs& a, uint32_t off) {
         if constexpr (TB % 4 == 2)
             atomic_add_elem<DT, ES>(p + (TB - 2), out[(TB - 2) / 4] & 0xFFFFu);
     } else {
-        store_partial<TB>(rd, off, out);
+        store_partial<TB, store_policy_for(NR)>(rd, off, out);
     }
 }
 
@@ -979,7 +984,7 @@ __device__ __forceinline__ void row_head(const KArgs& a, uint32_t off) {
 #pragma unroll
         for (int e = A; e < 16; e += 4) atomic_add_word<DT>(p + e, out[e / 4]);
     } else {
-        store_head<LO>(make_rsrc(a.dst, a.extent), off, out);
+        store_head<LO, store_policy_for(NR)>(make_rsrc(a.dst, a.extent), off, out);
     }
 }
 
@@ -1002,7 +1007,7 @@ __device__ __forceinline__ void row_tail_tile(const KArgs& a, uint32_t t) {
             u32x4 out[1];
             fold_slots<DT, OP, NR, 1>([&](uint32_t r) { return make_rsrc(a.src[r], a.extent); },
                                       a.nranks, off, out);
-            store_result<DT, SM>(a, make_rsrc(a.dst, a.extent), off[0], out[0]);
+            store_result<DT, SM, NR>(a, make_rsrc(a.dst, a.extent), off[0], out[0]);
             return;
         }
         const uint32_t off = h * a.ld_bytes + a.head_off;

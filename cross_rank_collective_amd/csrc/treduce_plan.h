@@ -160,29 +160,28 @@ constexpr int unroll_for(int nranks) {
 }
 constexpr int kElemUnroll = 4;     // elements per thread, element-wise path
 
-// Workgroups kept resident per CU for one-tile-per-block launches, from the
-// HBM bytes one tile moves (1 KiB per stream per slot row of the wave).
-// With every CU full the chip works on tens of thousands of scattered 1 KiB
-// runs at once; keeping a few tiles per CU resident, issued in order by the
+// Workgroups kept resident per CU for one-tile-per-block launches.  With
+// every CU full the chip works on tens of thousands of scattered 1 KiB runs
+// at once; keeping a few tiles per CU resident, issued in order by the
 // dispatcher, keeps the live window of every buffer compact.  The counts are
-// the best of sweeps on MI355X over 3-32 workgroups per CU, rank counts 1-32,
-// four element types and every walk: about 64-136 KiB in flight per CU for
-// the reduction and the ring, fewer for the in-place allreduce, whose
-// stores are half of its bytes (64-96 KiB).
-// The runtime rank loop keeps only one group of four ranks' loads in
-// flight per wave, so it wants more waves than its tile bytes suggest: 10
-// per CU (6 for the allreduce) measured best at N = 17-32 for bf16 Sum
-// (whose per-step rounding chain needs the most waves), f16 and i32.
-constexpr int wgs_per_cu_for(uint64_t tile_bytes, bool allreduce, bool runtime_loop) {
-    if (runtime_loop) return allreduce ? 6 : 10;
-    if (allreduce)
-        return tile_bytes <= 8u * 1024u ? 8 : (tile_bytes <= 16u * 1024u ? 5 : 3);
-    return tile_bytes <= 5u * 1024u    ? 16
-           : tile_bytes <= 7u * 1024u  ? 12
-           : tile_bytes <= 13u * 1024u ? 10
-           : tile_bytes <= 17u * 1024u ? 8
-                                       : 4;
+// the best of sweeps on MI355X over 4-16 workgroups per CU with dst written
+// to HBM on every call (a dst rewritten back to back stays in the 256 MB
+// Infinity Cache and favours other counts), rank counts 1-24, four element
+// types, the reduction and the ring:
+//   reduction, its copy and the ring: by rank count, 16 per CU up to 3 ranks
+//     down to 8 from 8 ranks on (about 48-128 KiB of loads in flight per CU);
+//   in-place allreduce, whose stores are half of its bytes: by the bytes a
+//     tile moves (2N x 1 KiB), 8 up to 8 KiB, 5 up to 16, 3 beyond;
+//   runtime rank loop: 10 (6 for the allreduce) -- it keeps only one group of
+//     four ranks' loads in flight per wave, so it wants more waves.
+constexpr int wgs_per_cu_reduce(int nranks) {
+    return nranks <= 3 ? 16 : nranks <= 5 ? 12 : nranks <= 7 ? 10 : 8;
 }
+constexpr int wgs_per_cu_allreduce(uint64_t tile_bytes) {
+    return tile_bytes <= 8u * 1024u ? 8 : (tile_bytes <= 16u * 1024u ? 5 : 3);
+}
+constexpr int kRuntimeLoopWgs = 10;
+constexpr int kRuntimeLoopAllreduceWgs = 6;
 // LDS is handed to workgroups in units of 1/128 of a CU's LDS (1280 bytes
 // on MI355X): measured, 32768-byte reservations fit 4 workgroups per CU and
 // 32000-byte ones 5, and the runtime's occupancy calculator, which assumes a

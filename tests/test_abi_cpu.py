@@ -137,22 +137,21 @@ def test_plan_paths():
 
 def test_plan_resident_workgroups():
     """Workgroups (one wave each) kept resident per CU by one-tile-per-block
-    launches, from the bytes one tile moves (1 KiB per stream per slot row):
-    16 up to 5 KiB, 12 up to 7, 10 up to 13, 8 up to 17; 10 for the runtime
-    rank loop; no limit for the element-wise kernel, persistent grids or on
-    request."""
-    assert _plan(n=16, srcs=A[:16], dtype=3).wgs_per_cu == 8   # 17 x 1 KiB
-    assert _plan(n=8, srcs=A[:8], dtype=1).wgs_per_cu == 10    # 9 x 1 KiB
-    assert _plan(n=12, srcs=A[:12]).wgs_per_cu == 10           # 13 x 1 KiB
-    assert _plan(n=6, srcs=A[:6]).wgs_per_cu == 12             # 7 x 1 KiB
-    assert _plan(n=5, srcs=A[:5]).wgs_per_cu == 12             # 6 x 1 KiB
-    assert _plan(n=4, srcs=A[:4]).wgs_per_cu == 16             # 5 x 1 KiB
-    assert _plan(n=2, srcs=A[:2]).wgs_per_cu == 12             # 3 x 2 KiB (2 slots per thread)
-    assert _plan(n=1).wgs_per_cu == 16                         # copy: 2 x 2 KiB
+    launches, by rank count: 16 up to 3 ranks, 12 at 4-5, 10 at 6-7, 8 from
+    8 on; 10 for the runtime rank loop; no limit for the element-wise
+    kernel, persistent grids or on request."""
+    assert _plan(n=16, srcs=A[:16], dtype=3).wgs_per_cu == 8
+    assert _plan(n=8, srcs=A[:8], dtype=1).wgs_per_cu == 8
+    assert _plan(n=12, srcs=A[:12]).wgs_per_cu == 8
+    assert _plan(n=6, srcs=A[:6]).wgs_per_cu == 10
+    assert _plan(n=5, srcs=A[:5]).wgs_per_cu == 12
+    assert _plan(n=4, srcs=A[:4]).wgs_per_cu == 12
+    assert _plan(n=2, srcs=A[:2]).wgs_per_cu == 16
+    assert _plan(n=1).wgs_per_cu == 16                         # copy
     assert _plan(n=17, srcs=A[:17]).wgs_per_cu == 10           # runtime rank loop
     info = _plan(n=64, srcs=A[:64])
     assert (info.wgs_per_cu, info.slots_per_thread) == (10, 1)
-    assert _plan(srcs=[A[0], A[1] + 4]).wgs_per_cu == 12       # unaligned: same rule
+    assert _plan(srcs=[A[0], A[1] + 4]).wgs_per_cu == 16       # unaligned: same rule
     t = B.tuning(flags=B.PTORED_FORCE_ELEMENTWISE)
     assert _plan(tuning=t).wgs_per_cu == 0                     # element-wise
     assert _plan(tuning=B.tuning(flags=B.PTORED_FULL_OCCUPANCY)).wgs_per_cu == 0
