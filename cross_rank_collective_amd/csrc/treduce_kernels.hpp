@@ -27,7 +27,7 @@
 // block-cyclic walk).  By default G equals the tile count -- one tile per
 // block, handed out in order by the hardware dispatcher, round-robin over
 // the XCDs, as blocks retire -- and the host keeps only 3-16 blocks resident
-// per CU (an LDS reservation, by the bytes a tile moves), so the tiles in
+// per CU (an LDS reservation, by rank count), so the tiles in
 // flight cover a compact window of every buffer; a smaller persistent grid
 // can be requested.  A block is one wave: its U * 64 slots are consecutive
 // and lane l takes slots l, l+64, ..., so every wave instruction moves

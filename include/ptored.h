@@ -155,7 +155,7 @@ int ptored_treduce(const void* const* srcs, int nranks, int root, void* dst, int
 typedef struct ptored_tuning {
     uint32_t flags;          /* PTORED_FORCE_* and PTORED_NO_XCD_REMAP bits */
     int32_t blocks_per_cu;   /* 0 = one workgroup (one wave) per tile (default; 3-16 resident
-                                per compute unit, by the bytes a tile moves); > 0 = persistent
+                                per compute unit, by rank count); > 0 = persistent
                                 grid of that many workgroups per compute unit, in per-XCD
                                 bands; < 0 = persistent grid at the kernel's occupancy */
     int64_t max_launch_bytes; /* split a call into launches that touch at most this many
