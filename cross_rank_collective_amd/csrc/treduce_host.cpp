@@ -232,7 +232,7 @@ int make_plan(const void* const* ptrs, int nptrs, int nranks, int64_t valid_rows
             p.wgs_per_cu = wgs_per_cu_allreduce(2u * (uint64_t)nranks * kBlock * 16u *
                                                 (uint64_t)p.unroll);
         } else {
-            p.wgs_per_cu = wgs_per_cu_reduce(p.family == kFamCopy ? 1 : nranks);
+            p.wgs_per_cu = wgs_per_cu_reduce(p.family == kFamCopy ? 1 : nranks, p.esize);
         }
     }
     const int64_t vec = p.vec_elems;

@@ -169,13 +169,15 @@ constexpr int kElemUnroll = 4;     // elements per thread, element-wise path
 // Infinity Cache and favours other counts), rank counts 1-24, four element
 // types, the reduction and the ring:
 //   reduction, its copy and the ring: by rank count, 16 per CU up to 3 ranks
-//     down to 8 from 8 ranks on (about 48-128 KiB of loads in flight per CU);
+//     down to 8 from 8 ranks on, and 6 from 12 ranks on for 4-byte types
+//     (about 48-128 KiB of loads in flight per CU; the 2-byte types, whose
+//     slots hold twice the elements to fold, keep 8 there);
 //   in-place allreduce, whose stores are half of its bytes: by the bytes a
 //     tile moves (2N x 1 KiB), 8 up to 8 KiB, 5 up to 16, 3 beyond;
 //   runtime rank loop: 10 (6 for the allreduce) -- it keeps only one group of
 //     four ranks' loads in flight per wave, so it wants more waves.
-constexpr int wgs_per_cu_reduce(int nranks) {
-    return nranks <= 3 ? 16 : nranks <= 5 ? 12 : nranks <= 7 ? 10 : 8;
+constexpr int wgs_per_cu_reduce(int nranks, int esize) {
+    return nranks <= 3 ? 16 : nranks <= 5 ? 12 : nranks <= 7 ? 10 : (nranks >= 12 && esize == 4) ? 6 : 8;
 }
 constexpr int wgs_per_cu_allreduce(uint64_t tile_bytes) {
     return tile_bytes <= 8u * 1024u ? 8 : (tile_bytes <= 16u * 1024u ? 5 : 3);

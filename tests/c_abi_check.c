@@ -34,7 +34,7 @@ int main(void) {
     CHECK(ptored_treduce_plan(srcs, 16, 0, dst, 4096, 4096, 4096, 4096, 4096, PTORED_I32,
                               PTORED_SUM, NULL, &info) == PTORED_OK);
     CHECK(info.path == PTORED_PATH_VEC_FIXED && info.rows_mode == 0 && info.launches == 1);
-    CHECK(info.vec_elems == 4 && info.slots == 4096 * 1024 && info.wgs_per_cu == 8);
+    CHECK(info.vec_elems == 4 && info.slots == 4096 * 1024 && info.wgs_per_cu == 6);
     CHECK(info.lead == 0);
     ptored_tuning t = {PTORED_FORCE_RUNTIME_N | PTORED_FULL_OCCUPANCY, 0, 0};
     CHECK(ptored_treduce_plan(srcs, 17, 3, dst, 8191, 12287, 12288, 8191, 12287, PTORED_F16,

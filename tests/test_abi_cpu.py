@@ -138,11 +138,14 @@ def test_plan_paths():
 def test_plan_resident_workgroups():
     """Workgroups (one wave each) kept resident per CU by one-tile-per-block
     launches, by rank count: 16 up to 3 ranks, 12 at 4-5, 10 at 6-7, 8 from
-    8 on; 10 for the runtime rank loop; no limit for the element-wise
-    kernel, persistent grids or on request."""
-    assert _plan(n=16, srcs=A[:16], dtype=3).wgs_per_cu == 8
+    8 on, 6 from 12 on for 4-byte types; 10 for the runtime rank loop; no
+    limit for the element-wise kernel, persistent grids or on request."""
+    assert _plan(n=16, srcs=A[:16], dtype=3).wgs_per_cu == 6
+    assert _plan(n=16, srcs=A[:16], dtype=1).wgs_per_cu == 8
     assert _plan(n=8, srcs=A[:8], dtype=1).wgs_per_cu == 8
-    assert _plan(n=12, srcs=A[:12]).wgs_per_cu == 8
+    assert _plan(n=11, srcs=A[:11]).wgs_per_cu == 8
+    assert _plan(n=12, srcs=A[:12]).wgs_per_cu == 6
+    assert _plan(n=12, srcs=A[:12], dtype=2).wgs_per_cu == 8
     assert _plan(n=6, srcs=A[:6]).wgs_per_cu == 10
     assert _plan(n=5, srcs=A[:5]).wgs_per_cu == 12
     assert _plan(n=4, srcs=A[:4]).wgs_per_cu == 12
