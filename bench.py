@@ -714,8 +714,10 @@ def main() -> int:
                     help="ptored tuning flags of the named workload's calls (PTORED_* bits, "
                          "e.g. 0x200 = per-rank push-with-add); 0 = automatic")
     ap.add_argument("--sets", type=int, default=0,
-                    help="input sets the steps rotate over (0 = enough to defeat the "
-                         "Infinity Cache when one set fits in it)")
+                    help="input sets and dsts the steps rotate over (0 = automatic: input "
+                         "sets rotated when one set fits in the Infinity Cache, and the "
+                         "buffers a step writes rotated until 512 MiB are written between "
+                         "two uses of one, so that every step reads from and writes to HBM)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM-traffic summaries from two rocprofv3 --pmc runs")
     ap.add_argument("--summarize-trace", metavar="DIR",
