@@ -514,6 +514,29 @@ def time_steps(torch, stream, step, steps: int, warmup: int):
     return ms_step, sorted(a_ev.elapsed_time(b_ev) for a_ev, b_ev in marks)
 
 
+def rotation(w, mode: str, sets_arg: int = 0):
+    """(input sets, dsts, residency) the steps of one entry rotate over.
+    Automatic (sets_arg <= 0): input sets when one set fits in the Infinity
+    Cache, until the steps touch ROTATE_BYTES; the buffers a step writes --
+    dst, or the sources themselves in the in-place modes -- until
+    WRITE_ROTATE_BYTES are written between two uses of one.  sets_arg > 0:
+    exactly that many of each.  residency is "hbm" when every step reads
+    from and writes to HBM."""
+    buf_bytes = w.buffer_elems * w.esize
+    set_bytes = (2 if mode == "memcpy" else w.nranks + 1) * buf_bytes
+    in_place = mode in ("allreduce", "reduce_scatter_ring")
+    written = w.nranks * buf_bytes if mode == "allreduce" else buf_bytes
+    nsets, ndst = sets_arg, sets_arg
+    if sets_arg <= 0:
+        nsets = 1 if set_bytes >= MALL_BYTES else min(MAX_SETS, -(-ROTATE_BYTES // set_bytes))
+        if in_place:
+            nsets = max(nsets, -(-WRITE_ROTATE_BYTES // written))
+        ndst = nsets if in_place else max(nsets, min(MAX_DSTS, -(-WRITE_ROTATE_BYTES // written)))
+    reads_hbm = set_bytes >= MALL_BYTES or nsets * set_bytes >= ROTATE_BYTES
+    writes_hbm = (nsets if in_place else ndst) * written >= WRITE_ROTATE_BYTES
+    return nsets, ndst, "hbm" if reads_hbm and writes_hbm else "cache-resident"
+
+
 def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg: int, dev,
               srcs, flags: int = 0):
     """Time one (workload, op, mode) on the GPU; returns its entry and the
@@ -530,24 +553,14 @@ def run_entry(torch, B, w, op: str, mode: str, steps: int, warmup: int, sets_arg
     # buffers a step writes -- dst, or the sources themselves for the
     # in-place modes -- rotate until WRITE_ROTATE_BYTES are written between
     # two uses of one.  --sets S instead takes exactly S sets and S dsts.
-    set_bytes = (2 if mode == "memcpy" else w.nranks + 1) * buf_bytes
     in_place = mode in ("allreduce", "reduce_scatter_ring")
-    written = w.nranks * buf_bytes if mode == "allreduce" else buf_bytes
-    nsets, ndst = sets_arg, sets_arg
-    if sets_arg <= 0:
-        nsets = 1 if set_bytes >= MALL_BYTES else min(MAX_SETS, -(-ROTATE_BYTES // set_bytes))
-        if in_place:
-            nsets = max(nsets, -(-WRITE_ROTATE_BYTES // written))
-        ndst = nsets if in_place else max(nsets, min(MAX_DSTS, -(-WRITE_ROTATE_BYTES // written)))
+    nsets, ndst, residency = rotation(w, mode, sets_arg)
     sets = [src_t] + [[t.clone() for t in src_t] for _ in range(nsets - 1)]
     dsts = [dst_t] + [dst_t.clone() for _ in range(ndst - 1)]
     # host pointer arrays built once, so the timed calls marshal only scalars
     set_ptrs = [B.pointer_array([t.data_ptr() for t in srcs_k]) for srcs_k in sets]
     dst_ptrs = [dst_k.data_ptr() for dst_k in dsts]
     cuda_stream = stream.cuda_stream
-    reads_hbm = set_bytes >= MALL_BYTES or nsets * set_bytes >= ROTATE_BYTES
-    writes_hbm = (nsets if in_place else ndst) * written >= WRITE_ROTATE_BYTES
-    residency = "hbm" if reads_hbm and writes_hbm else "cache-resident"
     tuning = B.tuning(flags=flags) if flags else None
     launches, launch = 1, None
     if mode == "treduce":

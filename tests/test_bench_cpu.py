@@ -157,3 +157,22 @@ def test_summarize_trace_pairs_each_entry_with_its_kernel(monkeypatch, tmp_path)
         assert vals["kernel_average_us"] == avg
         assert vals["kernel_average_within_ms_per_step"] == within
         assert "uuid u" in text
+
+
+def test_rotation_sends_every_step_to_hbm():
+    """Input sets rotate only when one set fits in the Infinity Cache; the
+    buffers a step writes rotate until 512 MiB are written between two uses
+    of one, so a dst rewritten back to back cannot stay in the cache."""
+    import bench
+    from cross_rank_collective_amd import workloads as W
+    head = W.find("n16_i32_4096x4096")
+    assert bench.rotation(head, "treduce") == (1, 8, "hbm")            # 64 MiB dst
+    assert bench.rotation(W.find("n8_bf16_8192x8192"), "treduce") == (1, 4, "hbm")
+    assert bench.rotation(W.find("n8_f16_8192x12288_valid8191x12287"), "treduce") == (1, 3, "hbm")
+    small = W.find("n4_f32_1024x1024_valid1000x1000")
+    assert bench.rotation(small, "treduce") == (52, 128, "hbm")        # 20 MiB sets, 4 MiB dsts
+    assert bench.rotation(head, "allreduce") == (1, 1, "hbm")          # writes all 16 buffers
+    assert bench.rotation(head, "reduce_scatter_ring") == (8, 8, "hbm")  # writes 64 MiB per step
+    assert bench.rotation(head, "accumulate_add") == (1, 8, "hbm")
+    assert bench.rotation(head, "treduce", 1) == (1, 1, "cache-resident")
+    assert bench.rotation(W.find("n2_f32_16x16"), "treduce")[2] == "cache-resident"
