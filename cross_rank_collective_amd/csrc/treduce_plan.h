@@ -173,14 +173,14 @@ constexpr int kElemUnroll = 4;     // elements per thread, element-wise path
 //     (about 48-128 KiB of loads in flight per CU; the 2-byte types, whose
 //     slots hold twice the elements to fold, keep 8 there);
 //   in-place allreduce, whose stores are half of its bytes: by the bytes a
-//     tile moves (2N x 1 KiB), 8 up to 8 KiB, 5 up to 16, 3 beyond;
+//     tile moves (2N x 1 KiB), 8 up to 8 KiB, 5 up to 16, 4 beyond;
 //   runtime rank loop: 10 (6 for the allreduce) -- it keeps only one group of
 //     four ranks' loads in flight per wave, so it wants more waves.
 constexpr int wgs_per_cu_reduce(int nranks, int esize) {
     return nranks <= 3 ? 16 : nranks <= 5 ? 12 : nranks <= 7 ? 10 : (nranks >= 12 && esize == 4) ? 6 : 8;
 }
 constexpr int wgs_per_cu_allreduce(uint64_t tile_bytes) {
-    return tile_bytes <= 8u * 1024u ? 8 : (tile_bytes <= 16u * 1024u ? 5 : 3);
+    return tile_bytes <= 8u * 1024u ? 8 : (tile_bytes <= 16u * 1024u ? 5 : 4);
 }
 constexpr int kRuntimeLoopWgs = 10;
 constexpr int kRuntimeLoopAllreduceWgs = 6;
