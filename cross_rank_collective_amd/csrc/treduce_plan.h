@@ -168,8 +168,9 @@ constexpr int kElemUnroll = 4;     // elements per thread, element-wise path
 // to HBM on every call (a dst rewritten back to back stays in the 256 MB
 // Infinity Cache and favours other counts), rank counts 1-24, four element
 // types, the reduction and the ring:
-//   reduction, its copy and the ring: by rank count, 16 per CU up to 3 ranks
-//     down to 8 from 8 ranks on, and 6 from 12 ranks on for 4-byte types
+//   reduction, its copy, the ring and push-with-add (folded): by rank count,
+//     16 per CU up to 3 ranks down to 8 from 8 ranks on, and 6 from 12 ranks
+//     on for 4-byte types
 //     (about 48-128 KiB of loads in flight per CU; the 2-byte types, whose
 //     slots hold twice the elements to fold, keep 8 there);
 //   in-place allreduce, whose stores are half of its bytes: by the bytes a
